@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark: MLA decode over a latent cache on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--split-tokens T]
+
+A step is one pass of the whole decode hot path over one batch of synthetic
+DeepSeek-V3-shaped input already resident in HBM:
+    mla_absorb_query -> mla_decode_partial -> mla_combine -> mla_out_proj
+W untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisation.  Prints one JSON line.
+
+value = cache GB/s = (sum over sequences of cached tokens x 1,152 B) / time per step.
+The roofline object covers the dominant kernel (mla_decode_partial): its
+algorithmic bytes per launch over its average duration, timed with HIP events
+on the stream it runs on.  cpu_baseline times the fp64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+DEFAULT_WORKLOAD = "v3_b64_ragged_paged"
+DECODE_SOURCES = ("mla_latent_kv_31_amd/csrc/decode_mfma.hip", "mla_latent_kv_31_amd/csrc/generic.hip")
+
+
+def _kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, sha: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they match the source."""
+    p = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:  # noqa: BLE001 - informational only
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, on whole sequences of the same workload until `seconds` pass."""
+    import numpy as np
+
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = inp["dtype"]
+    w_uk = gen.as_f64(inp["w_uk"], dt)
+    w_uv = gen.as_f64(inp["w_uv"], dt)
+    toks, n = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        L = int(inp["lens"][b])
+        cache = gen.as_f64(O.gather_rows(inp["pool"], inp["page_table"], b, L), dt)
+        O.attention(gen.as_f64(inp["q_c"][b], dt), gen.as_f64(inp["q_r"][b], dt), L - 1, cache, w_uk, w_uv,
+                    w.d_c, base=w.rope_base)
+        toks += L
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    row_bytes = (w.d_c + w.d_r) * (2 if dt == "bf16" else 4)
+    return {"value": round(toks * row_bytes / el / 1e9, 6), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"first {n} of {w.batch} sequences ({toks} cached tokens, all {w.n_heads} heads, "
+                      f"unabsorbed fp64 NumPy) in {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--split-tokens", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    w = gen.WORKLOADS[args.workload]
+    if w.kind != "decode":
+        print(f"workload {w.name} is not a decode workload", file=sys.stderr)
+        return 2
+    split = args.split_tokens or w.split_tokens
+    inp = gen.make_decode_inputs(w)
+    dev = torch.device("cuda:0")
+    st = runner.DecodeStep(inp, split, dev)
+    lens = inp["lens"].astype(np.int64)
+    total_tokens = int(lens.sum())
+    row_bytes = (w.d_c + w.d_r) * 2
+    cache_bytes = total_tokens * row_bytes
+    flops_decode = total_tokens * (2 * w.n_heads * (w.d_c + w.d_r) + 2 * w.n_heads * w.d_c)
+    flops_proj = w.batch * 2 * w.n_heads * w.d_c * (w.d_k + w.d_v)
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        st.absorb()
+        ev[i][0].record(stream)
+        st.attend()
+        ev[i][1].record(stream)
+        st.combine()
+        st.out_proj()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    ms_decode = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    sha = _kernel_sha()
+    traffic = _traffic(w.name, sha)
+    achieved = cache_bytes / (ms_decode * 1e-3) / 1e9
+    rec = {
+        "metric": "MLA decode cache GB/s (V3 shape, 1 GPU)",
+        "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.n_heads, "d_c": w.d_c, "d_r": w.d_r,
+                   "d_k": w.d_k, "d_v": w.d_v, "page_size": w.page_size, "split_tokens": split,
+                   "n_splits": st.S, "cache_tokens": total_tokens, "seed": w.seed,
+                   "decode_kernel": "mfma" if st.uses_mfma() else "generic"},
+        "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "cache_tokens_per_s": round(total_tokens / (ms_step * 1e-3), 1),
+        "tflops": round((flops_decode + flops_proj) / (ms_step * 1e-3) / 1e12, 3),
+        "wall_s": round(t_wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_partial", "achieved": round(achieved, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms_decode, 6),
+                     "algorithmic_bytes_per_launch": cache_bytes, "kernel_source_sha": sha},
+        "roofline_mfma": {"achieved": round(flops_decode / (ms_decode * 1e-3) / 1e12, 3),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(flops_decode / (ms_decode * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * libmla -- weight-absorbed Multi-Head Latent Attention over a latent cache, for gfx950.
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [molayo] "Multi-Head Latent Attention (MLA)" (molayo1419.me)
+ *   [ase]    "MLA의 계산: KV를 펼치지 않고 Attention하기" (ai-systems-engineering.com)
+ *   [huny]   "DeepSeek Multi-Head Latent Attention(MLA) 아키텍처 해부 ..." (blog.huny.dev)
+ *
+ * Common rules for every entry point
+ *   - Device pointers are plain device addresses owned by the caller.  The library allocates
+ *     nothing, keeps no state between calls and retains no pointer after a call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the null stream).
+ *   - Host-visible arguments are validated before anything is launched; a failed check returns
+ *     an MLA_ERR_* code and touches no device memory.  A failed launch returns MLA_ERR_HIP.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *   - Device-resident values (seq_lens, page_table, positions) are trusted: out-of-range
+ *     values are undefined behaviour.  Cache slots past a sequence's length may hold any bits,
+ *     NaN included; results never depend on them.
+ *   - Every device pointer must be 16-byte aligned (MLA_ERR_ALIGN otherwise).
+ *   - Outputs are overwritten, never accumulated into.  Entry points are thread-safe.
+ *   - Tensors are dense row-major in the index order written next to them.
+ *   - Values of type "dtype" are float32 (MLA_F32) or bfloat16 bit patterns (MLA_BF16) as
+ *     selected by mla_dims.dtype; arithmetic accumulates in float32.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* a size or dimension is out of range or inconsistent */
+  MLA_ERR_DTYPE = 3,       /* unknown dtype code */
+  MLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  MLA_ERR_UNSUPPORTED = 5, /* well-formed but beyond what the kernels implement */
+  MLA_ERR_HIP = 6          /* a HIP runtime call or a kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Flags for mla_dims.flags. */
+#define MLA_FLAG_FORCE_GENERIC 1 /* use the dimension-generic kernels even where a tuned one exists */
+
+/* Model dimensions shared by every call.
+ * Cached row of one token: [c^KV (d_c) | k^R (d_r)], k^R already rotated at its position and
+ * shared by all heads ([huny] section 2, decoupled-RoPE principle; [ase] Fig. 1 caption). */
+typedef struct {
+  int32_t n_heads;  /* H */
+  int32_t d_c;      /* latent width */
+  int32_t d_r;      /* rotary width of the position query/key (even, may be 0) */
+  int32_t d_k;      /* content query/key width per head */
+  int32_t d_v;      /* value width per head */
+  float rope_base;  /* RoPE base; inverse frequencies base^(-2i/d_r) on interleaved pairs */
+  float sm_scale;   /* softmax scale; 0 selects 1/sqrt(d_k + d_r) ([ase] scale remark, Fig. 2) */
+  int32_t dtype;    /* mla_dtype of queries, weights, cache rows and q_hat */
+  int32_t flags;    /* MLA_FLAG_* */
+} mla_dims;
+
+/* A paged latent cache ([molayo] key concept 5: a page table holding latent rows).
+ * Token t of sequence b lives at pool[page_table[b*max_pages + t/page_size]][t % page_size].
+ * A contiguous cache is the identity page table. */
+typedef struct {
+  const void* pool;          /* device, dtype [num_pages, page_size, d_c + d_r] */
+  const int32_t* page_table; /* device [batch, max_pages]; entries past a sequence's pages unused */
+  const int32_t* seq_lens;   /* device [batch]; valid tokens per sequence, current token included */
+  int32_t batch;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t num_pages;
+} mla_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_str(mla_status s);
+
+/* Absorbed query ([ase] "Key 투영을 Query 쪽으로 옮기기", Fig. 3 equation; [ase] Fig. 1 for the
+ * rotated position query; [molayo] key concept 1):
+ *   q_hat[r,h,:] = [ q_c[r,h,:] . W_UK[h]^T  |  RoPE_{pos[r]}(q_r[r,h,:]) ] * (sm_scale * log2(e))
+ * The product with log2(e) makes later scores base-2 logits; lse outputs stay natural-log.
+ *   q_c   device dtype [rows, H, d_k]
+ *   q_r   device dtype [rows, H, d_r]   (unrotated; may be NULL when d_r == 0)
+ *   w_uk  device dtype [H, d_c, d_k]
+ *   pos   device int32 [rows]           absolute position of each query row
+ *   q_hat device dtype [rows, H, d_c + d_r]  (output)                                          */
+mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q_r, const void* w_uk,
+                            const int32_t* pos, int32_t rows, void* q_hat, void* stream);
+
+/* Number of split-K chunks per sequence: ceil(max_len / split_tokens), at least 1. */
+int32_t mla_decode_num_splits(int32_t max_len, int32_t split_tokens);
+
+/* Nonzero when mla_decode_partial / mla_prefill_chunk take the MFMA kernels for these arguments. */
+int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32_t split_tokens);
+int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache);
+
+/* Split-K decode over the latent cache, one query token per sequence (the newest, at position
+ * seq_lens[b]-1).  Chunk i of sequence b covers tokens [i*split_tokens, (i+1)*split_tokens)
+ * intersected with [0, seq_lens[b]).  For each chunk and head it writes the chunk-local softmax
+ * result ([ase] Fig. 2 scores over the 576-wide concatenation; Fig. 4: the weighted latent
+ * z = a.C, the rotary part is never summed):
+ *   o_part[b,i,h,:] = sum_t softmax_t(s) c_t  (normalised within the chunk)
+ *   lse_part[b,i,h] = ln sum_t exp(s_t)        with s_t = q_hat . row_t / log2(e)
+ * An empty chunk writes o_part = 0 and lse_part = -inf.
+ *   q_hat    device dtype [batch, H, d_c + d_r]   (as written by mla_absorb_query)
+ *   max_len  host bound >= every seq_lens[b]; sets S = mla_decode_num_splits(max_len, split_tokens)
+ *   split_tokens  > 0 and a multiple of cache->page_size
+ *   o_part   device float [batch, S, H, d_c]
+ *   lse_part device float [batch, S, H]                                                          */
+mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                              int32_t max_len, int32_t split_tokens, float* o_part, float* lse_part,
+                              void* stream);
+
+/* Log-sum-exp merge of split-K partials: LSE = ln sum_i exp(lse_i),
+ * z = sum_i exp(lse_i - LSE) o_i.  Over any split this equals the single-pass softmax of
+ * [ase] Fig. 2.  All chunks empty gives z = 0 and lse = -inf.
+ *   o_part   device float [batch, n_splits, H, d_c]
+ *   lse_part device float [batch, n_splits, H]
+ *   z        device float [batch, H, d_c]       (output)
+ *   lse      device float [batch, H] or NULL   (output)                                          */
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const float* o_part,
+                       const float* lse_part, float* z, float* lse, void* stream);
+
+/* Value up-projection applied once after the weighted sum ([ase] "Value 투영을 가중합 뒤로
+ * 옮기기", Fig. 4 equation; [huny] section 2, value absorption):
+ *   out[r,h,:] = z[r,h,:] . W_UV[h]
+ *   z    device float [rows, H, d_c]
+ *   w_uv device dtype [H, d_c, d_v]
+ *   out  device float [rows, H, d_v]   (output)                                                  */
+mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,
+                        void* stream);
+
+/* Causal multi-query attention for a chunk of new tokens whose rows are already in the cache
+ * ([ase] causal-mask remark after Fig. 2; [molayo] chunked prefill).  Query i of sequence b sits
+ * at absolute position q_start[b] + i and reads tokens t <= q_start[b] + i, t < seq_lens[b].
+ *   q_hat   device dtype [batch, q_len, H, d_c + d_r]
+ *   q_start device int32 [batch]
+ *   z       device float [batch, q_len, H, d_c]   (output, normalised)
+ *   lse     device float [batch, q_len, H] or NULL (output, natural log)                         */
+mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t q_len,
+                             const int32_t* q_start, float* z, float* lse, void* stream);
+
+/* Query side of one layer ([ase] "현재 토큰의 Query 만들기", Fig. 1; [molayo] query compression):
+ *   c^Q = h . W_DQ;  q_c[r,h,:] = c^Q . W_UQ[h];  q_r[r,h,:] = c^Q . W_QR[h]  (unrotated)
+ *   h    device dtype [rows, d_model];  w_dq dtype [d_model, d_cq]
+ *   w_uq dtype [H, d_cq, d_k];  w_qr dtype [H, d_cq, d_r]
+ *   q_c  dtype [rows, H, d_k], q_r dtype [rows, H, d_r]   (outputs)                              */
+mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq, const void* h,
+                             const void* w_dq, const void* w_uq, const void* w_qr, int32_t rows,
+                             void* q_c, void* q_r, void* stream);
+
+/* Cache write for new tokens ([molayo] formal definition, compression; [huny] section 2,
+ * decoupled RoPE; [ase] Fig. 1 note on the latent norm):
+ *   c = h . W_DKV, optionally RMS-normalised (unit gain) when rms_eps > 0;
+ *   k^R = RoPE_{pos}(h . W_KR); row [c | k^R] stored at token `positions[r]` of sequence
+ *   `seq_ids[r]` through the page table of `cache` (cache->pool is written).
+ *   h device dtype [rows, d_model]; w_dkv dtype [d_model, d_c]; w_kr dtype [d_model, d_r]
+ *   seq_ids, positions device int32 [rows]                                                       */
+mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
+                         const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                         const int32_t* positions, int32_t rows, float rms_eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,215 @@
+// C ABI of libmla: argument validation and kernel dispatch.  Every check here runs on the host
+// before any HIP call, so a rejected call has no side effects.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "mla.h"
+
+namespace mla {
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status check_dims(const mla_dims* dims, Dims* out) {
+  if (!dims) return MLA_ERR_NULL;
+  if (dims->dtype != MLA_F32 && dims->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (dims->n_heads < 1 || dims->d_c < 1 || dims->d_r < 0 || (dims->d_r & 1) || dims->d_k < 1 || dims->d_v < 1)
+    return MLA_ERR_SHAPE;
+  if (dims->n_heads > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!(dims->sm_scale >= 0.f) || !isfinite(dims->sm_scale)) return MLA_ERR_SHAPE;
+  if (dims->d_r > 0 && !(dims->rope_base > 0.f && isfinite(dims->rope_base))) return MLA_ERR_SHAPE;
+  if (dims->d_c > kGenericMaxDc || dims->d_c + dims->d_r > kGenericMaxRow || dims->d_k > kGenericMaxDk ||
+      dims->d_v > 4096)
+    return MLA_ERR_UNSUPPORTED;
+  out->H = dims->n_heads;
+  out->dc = dims->d_c;
+  out->dr = dims->d_r;
+  out->dk = dims->d_k;
+  out->dv = dims->d_v;
+  out->rope_base = dims->rope_base;
+  out->sm_scale = dims->sm_scale > 0.f ? dims->sm_scale : 1.0f / sqrtf(float(dims->d_k + dims->d_r));
+  out->dtype = dims->dtype;
+  return MLA_OK;
+}
+
+mla_status check_cache(const mla_cache* cache, Cache* out) {
+  if (!cache) return MLA_ERR_NULL;
+  if (!cache->pool || !cache->page_table || !cache->seq_lens) return MLA_ERR_NULL;
+  if (!aligned16(cache->pool) || !aligned16(cache->page_table) || !aligned16(cache->seq_lens)) return MLA_ERR_ALIGN;
+  if (cache->batch < 0 || cache->page_size < 1 || cache->max_pages < 1 || cache->num_pages < 1)
+    return MLA_ERR_SHAPE;
+  if (cache->batch > 65535) return MLA_ERR_UNSUPPORTED;
+  out->pool = cache->pool;
+  out->page_table = cache->page_table;
+  out->seq_lens = cache->seq_lens;
+  out->batch = cache->batch;
+  out->page_size = cache->page_size;
+  out->max_pages = cache->max_pages;
+  out->num_pages = cache->num_pages;
+  return MLA_OK;
+}
+
+mla_status ptr_ok(const void* p) {
+  if (!p) return MLA_ERR_NULL;
+  return aligned16(p) ? MLA_OK : MLA_ERR_ALIGN;
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+#define MLA_TRY(expr)                 \
+  do {                                \
+    mla_status _st = (expr);          \
+    if (_st != MLA_OK) return _st;    \
+  } while (0)
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size or dimension is out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown dtype code";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: well-formed but beyond the implemented limits";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown mla_status";
+}
+
+int32_t mla_decode_num_splits(int32_t max_len, int32_t split_tokens) {
+  if (split_tokens < 1 || max_len < 0) return -1;
+  const int64_t s = (int64_t(max_len) + split_tokens - 1) / split_tokens;
+  return int32_t(s < 1 ? 1 : s);
+}
+
+int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32_t split_tokens) {
+  (void)dims;
+  (void)cache;
+  (void)split_tokens;
+  return 0;
+}
+
+int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache) {
+  (void)dims;
+  (void)cache;
+  return 0;
+}
+
+mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q_r, const void* w_uk,
+                            const int32_t* pos, int32_t rows, void* q_hat, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (rows < 0) return MLA_ERR_SHAPE;
+  MLA_TRY(ptr_ok(q_c));
+  if (d.dr > 0) MLA_TRY(ptr_ok(q_r));
+  MLA_TRY(ptr_ok(w_uk));
+  MLA_TRY(ptr_ok(pos));
+  MLA_TRY(ptr_ok(q_hat));
+  if (rows == 0) return MLA_OK;
+  return hip_status(launch_absorb_generic(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
+}
+
+mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t max_len,
+                              int32_t split_tokens, float* o_part, float* lse_part, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  MLA_TRY(ptr_ok(q_hat));
+  MLA_TRY(ptr_ok(o_part));
+  MLA_TRY(ptr_ok(lse_part));
+  if (split_tokens < 1 || split_tokens % c.page_size != 0) return MLA_ERR_SHAPE;
+  if (max_len < 0 || int64_t(max_len) > int64_t(c.max_pages) * c.page_size) return MLA_ERR_SHAPE;
+  const int S = mla_decode_num_splits(max_len, split_tokens);
+  if (c.batch == 0) return MLA_OK;
+  return hip_status(launch_decode_generic(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
+}
+
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const float* o_part,
+                       const float* lse_part, float* z, float* lse, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (batch < 0 || n_splits < 1) return MLA_ERR_SHAPE;
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(o_part));
+  MLA_TRY(ptr_ok(lse_part));
+  MLA_TRY(ptr_ok(z));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (batch == 0) return MLA_OK;
+  return hip_status(launch_combine_generic(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
+}
+
+mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,
+                        void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (rows < 0) return MLA_ERR_SHAPE;
+  if (rows > 65535) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(z));
+  MLA_TRY(ptr_ok(w_uv));
+  MLA_TRY(ptr_ok(out));
+  if (rows == 0) return MLA_OK;
+  return hip_status(launch_out_proj_generic(d, z, w_uv, rows, out, (hipStream_t)stream));
+}
+
+mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t q_len,
+                             const int32_t* q_start, float* z, float* lse, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  if (q_len < 0) return MLA_ERR_SHAPE;
+  MLA_TRY(ptr_ok(q_hat));
+  MLA_TRY(ptr_ok(q_start));
+  MLA_TRY(ptr_ok(z));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (c.batch == 0 || q_len == 0) return MLA_OK;
+  return hip_status(launch_prefill_generic(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream));
+}
+
+mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq, const void* h, const void* w_dq,
+                             const void* w_uq, const void* w_qr, int32_t rows, void* q_c, void* q_r, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (d_model < 1 || d_cq < 1 || rows < 0) return MLA_ERR_SHAPE;
+  if (d_model + d_cq > 8192) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(h));
+  MLA_TRY(ptr_ok(w_dq));
+  MLA_TRY(ptr_ok(w_uq));
+  MLA_TRY(ptr_ok(q_c));
+  if (d.dr > 0) {
+    MLA_TRY(ptr_ok(w_qr));
+    MLA_TRY(ptr_ok(q_r));
+  }
+  if (rows == 0) return MLA_OK;
+  return hip_status(launch_project_query(d, d_model, d_cq, h, w_dq, w_uq, w_qr, rows, q_c, q_r, (hipStream_t)stream));
+}
+
+mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
+                         const void* w_dkv, const void* w_kr, const int32_t* seq_ids, const int32_t* positions,
+                         int32_t rows, float rms_eps, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  if (d_model < 1 || rows < 0 || !(rms_eps == rms_eps)) return MLA_ERR_SHAPE;
+  if (d_model + d.dc + d.dr > 8192) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(h));
+  MLA_TRY(ptr_ok(w_dkv));
+  if (d.dr > 0) MLA_TRY(ptr_ok(w_kr));
+  MLA_TRY(ptr_ok(seq_ids));
+  MLA_TRY(ptr_ok(positions));
+  if (rows == 0) return MLA_OK;
+  return hip_status(
+      launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
+}
+
+}  // extern "C"

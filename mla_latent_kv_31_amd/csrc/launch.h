@@ -1,0 +1,48 @@
+// Host-side launchers behind the C ABI.  Arguments are already validated by api.hip;
+// each launcher returns the HIP status of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+struct Dims {
+  int H, dc, dr, dk, dv;
+  float rope_base, sm_scale;
+  int dtype;
+  __host__ __device__ int W() const { return dc + dr; }
+};
+
+struct Cache {
+  const void* pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int batch, page_size, max_pages, num_pages;
+};
+
+// ---- dimension-generic kernels (any sizes within the documented limits; fp32 or bf16)
+constexpr int kGenericMaxDc = 1024;   // latent width handled by the generic decode/combine
+constexpr int kGenericMaxRow = 2048;  // d_c + d_r
+constexpr int kGenericMaxDk = 1024;
+
+hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
+                                 const int32_t* pos, int rows, void* q_hat, hipStream_t s);
+hipError_t launch_decode_generic(const Dims& d, const Cache& c, const void* q_hat, int n_splits,
+                                 int split_tokens, float* o_part, float* lse_part, hipStream_t s);
+hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_hat, int q_len,
+                                  const int32_t* q_start, float* z, float* lse, hipStream_t s);
+hipError_t launch_combine_generic(const Dims& d, int batch, int n_splits, const float* o_part,
+                                  const float* lse_part, float* z, float* lse, hipStream_t s);
+hipError_t launch_out_proj_generic(const Dims& d, const float* z, const void* w_uv, int rows, float* out,
+                                   hipStream_t s);
+hipError_t launch_project_query(const Dims& d, int d_model, int d_cq, const void* h, const void* w_dq,
+                                const void* w_uq, const void* w_qr, int rows, void* q_c, void* q_r,
+                                hipStream_t s);
+hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
+                            const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
+                            float rms_eps, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,135 @@
+"""Device buffers and call sequences for one decode step and one chunked-prefill call.
+
+This module only allocates device memory (through torch) and calls the C
+entry points in order; all arithmetic runs in libmla.so.
+
+Decode step (one query token per sequence):
+    mla_absorb_query -> mla_decode_partial -> mla_combine -> mla_out_proj
+Chunked prefill (q_len query tokens per sequence):
+    mla_absorb_query -> mla_prefill_chunk -> mla_out_proj
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def to_device(x: np.ndarray, device) -> torch.Tensor:
+    """Host array -> device tensor.  uint16 arrays are bfloat16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(x).to(device)
+
+
+def _torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def dims_for(w, flags: int = 0) -> L.MlaDims:
+    return L.dims(w.n_heads, w.d_c, w.d_r, w.d_k, w.d_v, dtype=L.MLA_BF16 if w.dtype == "bf16" else L.MLA_F32,
+                  rope_base=w.rope_base, sm_scale=0.0, flags=flags)
+
+
+class DecodeStep:
+    """All device buffers of one batched decode step; ``run()`` enqueues the four calls."""
+
+    def __init__(self, inp: dict, split_tokens: int, device="cuda:0", flags: int = 0, max_len: int | None = None):
+        w = inp["workload"]
+        self.w = w
+        self.device = torch.device(device)
+        self.d = dims_for(w, flags)
+        dev = self.device
+        self.q_c = to_device(inp["q_c"], dev)
+        self.q_r = to_device(inp["q_r"], dev)
+        self.w_uk = to_device(inp["w_uk"], dev)
+        self.w_uv = to_device(inp["w_uv"], dev)
+        self.pool = to_device(inp["pool"], dev)
+        self.page_table = to_device(inp["page_table"], dev)
+        self.lens = to_device(inp["lens"].astype(np.int32), dev)
+        self.pos = to_device(inp["pos"].astype(np.int32), dev)
+        self.B = int(inp["lens"].shape[0])
+        self.max_len = int(inp["lens"].max()) if max_len is None else int(max_len)
+        self.split_tokens = int(split_tokens)
+        self.S = L.mla_decode_num_splits(self.max_len, self.split_tokens)
+        H, W = w.n_heads, w.d_c + w.d_r
+        td = _torch_dtype(w.dtype)
+        self.q_hat = torch.empty((self.B, H, W), dtype=td, device=dev)
+        self.o_part = torch.empty((self.B, self.S, H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((self.B, self.S, H), dtype=torch.float32, device=dev)
+        self.z = torch.empty((self.B, H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.B, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.B, H, w.d_v), dtype=torch.float32, device=dev)
+        self.c = L.cache(self.pool, self.page_table, self.lens)
+
+    def uses_mfma(self) -> bool:
+        return L.mla_decode_uses_mfma(self.d, self.c, self.split_tokens)
+
+    def absorb(self, stream=None):
+        L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.pos, self.B, self.q_hat, stream)
+
+    def attend(self, stream=None):
+        L.mla_decode_partial(self.d, self.c, self.q_hat, self.max_len, self.split_tokens, self.o_part,
+                             self.lse_part, stream)
+
+    def combine(self, stream=None):
+        L.mla_combine(self.d, self.B, self.S, self.o_part, self.lse_part, self.z, self.lse, stream)
+
+    def out_proj(self, stream=None):
+        L.mla_out_proj(self.d, self.z, self.w_uv, self.B, self.out, stream)
+
+    def run(self, stream=None):
+        self.absorb(stream)
+        self.attend(stream)
+        self.combine(stream)
+        self.out_proj(stream)
+
+
+class PrefillStep:
+    """Device buffers of one chunked-prefill call; ``run()`` enqueues absorb, prefill, out_proj."""
+
+    def __init__(self, inp: dict, device="cuda:0", flags: int = 0):
+        w = inp["workload"]
+        self.w = w
+        self.device = torch.device(device)
+        self.d = dims_for(w, flags)
+        dev = self.device
+        self.q_c = to_device(inp["q_c"], dev)
+        self.q_r = to_device(inp["q_r"], dev)
+        self.w_uk = to_device(inp["w_uk"], dev)
+        self.w_uv = to_device(inp["w_uv"], dev)
+        self.pool = to_device(inp["pool"], dev)
+        self.page_table = to_device(inp["page_table"], dev)
+        self.lens = to_device(inp["lens"].astype(np.int32), dev)
+        self.q_start = to_device(inp["q_start"].astype(np.int32), dev)
+        B, Sq = inp["q_c"].shape[0], inp["q_c"].shape[1]
+        self.B, self.Sq = int(B), int(Sq)
+        pos = (inp["q_start"][:, None] + np.arange(Sq)[None, :]).astype(np.int32).reshape(-1)
+        self.pos = to_device(pos, dev)
+        H, W = w.n_heads, w.d_c + w.d_r
+        td = _torch_dtype(w.dtype)
+        self.q_hat = torch.empty((self.B, self.Sq, H, W), dtype=td, device=dev)
+        self.z = torch.empty((self.B, self.Sq, H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
+        self.c = L.cache(self.pool, self.page_table, self.lens)
+
+    def uses_mfma(self) -> bool:
+        return L.mla_prefill_uses_mfma(self.d, self.c)
+
+    def absorb(self, stream=None):
+        L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.pos, self.B * self.Sq, self.q_hat, stream)
+
+    def attend(self, stream=None):
+        L.mla_prefill_chunk(self.d, self.c, self.q_hat, self.Sq, self.q_start, self.z, self.lse, stream)
+
+    def out_proj(self, stream=None):
+        L.mla_out_proj(self.d, self.z, self.w_uv, self.B * self.Sq, self.out, stream)
+
+    def run(self, stream=None):
+        self.absorb(stream)
+        self.attend(stream)
+        self.out_proj(stream)

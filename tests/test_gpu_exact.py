@@ -1,0 +1,156 @@
+"""Exactness of split-K indexing and length masking on the GPU.
+
+* count test: with a zero query every score is 0, so each chunk's softmax sum is exactly its
+  number of valid tokens; exp(lse_part) must round to that integer, empty chunks give -inf/0.
+* spike test: one token scores 2^128 above the rest, so z must equal that token's latent; a
+  chunk or length boundary off by one gives an O(1) error instead of a 1/len-sized one.
+* poison test: NaN / Inf / zero in every slot a correct reader never touches must give
+  bitwise-identical outputs.
+* permutation test: two physical page layouts of one logical cache give bitwise-identical outputs.
+* re-runs are bitwise deterministic; split sizes agree to fp32 rounding.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_31_amd as M
+from mla_latent_kv_31_amd import runner
+from mla_workloads import gen
+from parity import note
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+V3 = dict(n_heads=128, d_c=512, d_r=64, d_k=128, d_v=128)
+
+
+def _w(batch, seed=21, random_pages=True):
+    return gen.Workload(name="exact", seed=seed, kind="decode", batch=batch, random_pages=random_pages, **V3)
+
+
+def _np(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def _run_partial(inp, split, q_hat_np=None, flags=0, max_len=None):
+    st = runner.DecodeStep(inp, split, DEV, flags=flags, max_len=max_len)
+    if q_hat_np is None:
+        st.absorb()
+    else:
+        st.q_hat.copy_(runner.to_device(q_hat_np, DEV))
+    st.attend()
+    st.combine()
+    torch.cuda.synchronize()
+    return st
+
+
+PATHS = [0, M.MLA_FLAG_FORCE_GENERIC]
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("split", [64, 128, 512])
+def test_count(split, flags):
+    lens = [1, 2, 63, 64, 65, 127, 128, 129, 500, 1000, 1024, 1025]
+    note(f"count split={split} flags={flags}")
+    inp = gen.make_decode_inputs(_w(len(lens)), lens=np.array(lens, np.int32), fill="nan")
+    q0 = np.zeros((len(lens), 128, 576), np.uint16)
+    st = _run_partial(inp, split, q0, flags=flags)
+    lse_p, o_p = _np(st.lse_part), _np(st.o_part)
+    for b, L in enumerate(lens):
+        for i in range(st.S):
+            cnt = max(0, min(L, (i + 1) * split) - i * split)
+            if cnt == 0:
+                assert np.all(lse_p[b, i] == -np.inf), (b, i)
+                assert np.all(o_p[b, i] == 0.0), (b, i)
+                continue
+            e = np.exp(lse_p[b, i].astype(np.float64))
+            assert np.all(np.rint(e) == cnt), (b, i, cnt, e[:4])
+            assert np.max(np.abs(e - cnt)) <= 1e-4 * cnt, (b, i)
+    # whole-sequence count through the combine
+    assert np.all(np.rint(np.exp(_np(st.lse).astype(np.float64))) == np.array(lens)[:, None])
+
+
+def _spike_inputs(cases, seed=31):
+    """cases: list of (length, spike position).  Column 0 of every latent is 0 except the spike
+    token's (8.0); the query is 16 on that column only (base-2 logit 128 for the spike)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for L, t in cases:
+        c = rng.standard_normal((L, 576)).astype(np.float32)
+        c[:, 0] = 0.0
+        c[t, 0] = 8.0
+        rows.append(gen.bf16_bits(c))
+    w = _w(len(cases), seed=seed)
+    lens = np.array([L for L, _ in cases], np.int32)
+    inp = gen.make_decode_inputs(w, lens=lens, latent_rows=rows, fill="nan")
+    q = np.zeros((len(cases), 128, 576), np.float32)
+    q[:, :, 0] = 16.0
+    return inp, gen.bf16_bits(q), rows
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("split", [64, 128, 256])
+def test_spike_at_every_boundary(split, flags):
+    cases = []
+    for L in (1, 64, 65, 200, 1000, 1025):
+        ts = {0, L - 1}
+        for i in range(0, -(-L // split)):
+            ts |= {i * split, i * split + split - 1, i * split + 63, i * split + 64}
+        cases += [(L, t) for t in sorted(ts) if 0 <= t < L]
+    note(f"spike split={split} flags={flags} cases={len(cases)}")
+    inp, q, rows = _spike_inputs(cases)
+    st = _run_partial(inp, split, q, flags=flags)
+    z, lse = _np(st.z), _np(st.lse)
+    for b, (L, t) in enumerate(cases):
+        want = gen.bf16_from_bits(rows[b][t, :512]).astype(np.float64)
+        err = np.max(np.abs(z[b] - want[None]))
+        assert err <= 1e-5, f"len {L} spike {t}: z off by {err}"
+        assert np.allclose(lse[b], 128.0 * np.log(2.0), atol=1e-4), (L, t, lse[b, :2])
+
+
+@pytest.mark.parametrize("flags", PATHS)
+def test_poison_bitwise(flags):
+    lens = np.array([1, 63, 64, 65, 700, 1234, 4000], np.int32)
+    note(f"poison flags={flags}")
+    outs = []
+    for fill in ("zero", "nan", "inf"):
+        inp = gen.make_decode_inputs(_w(len(lens)), lens=lens, fill=fill, spare_pages=16)
+        st = _run_partial(inp, 128, flags=flags)
+        st.out_proj()
+        torch.cuda.synchronize()
+        outs.append([_np(x).copy() for x in (st.o_part, st.lse_part, st.z, st.lse, st.out)])
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("flags", PATHS)
+def test_page_permutation_bitwise_and_determinism(flags):
+    lens = np.array([5, 640, 1999, 3000], np.int32)
+    note(f"permutation flags={flags}")
+    res = []
+    for rp in (False, True):
+        inp = gen.make_decode_inputs(_w(len(lens), random_pages=rp), lens=lens, fill="zero", random_pages=rp)
+        st = _run_partial(inp, 256, flags=flags)
+        res.append([_np(x).copy() for x in (st.o_part, st.lse_part, st.z, st.lse)])
+        st.attend()
+        st.combine()
+        torch.cuda.synchronize()
+        again = [_np(x) for x in (st.o_part, st.lse_part, st.z, st.lse)]
+        for a, b in zip(res[-1], again):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "re-run differs"
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "page layout changes the result"
+
+
+def test_split_invariance():
+    lens = np.array([3000, 70, 4096], np.int32)
+    note("split invariance")
+    inp = gen.make_decode_inputs(_w(len(lens), seed=41), lens=lens)
+    zs = []
+    for split in (64, 128, 512, 4096):
+        st = _run_partial(inp, split)
+        zs.append((_np(st.z).copy(), _np(st.lse).copy()))
+    for z, lse in zs[1:]:
+        assert np.max(np.abs(z - zs[0][0])) <= 1e-3 * np.sqrt(np.mean(zs[0][0] ** 2))
+        assert np.max(np.abs(lse - zs[0][1])) <= 1e-3

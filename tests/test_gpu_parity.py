@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded inputs.
+
+Every workload of the table runs at its full size in the launch configuration the benchmark
+times; outputs the oracle can afford are compared in full (toy, batch-1 4k, small V3 shapes),
+the large workloads on sampled (sequence, head) or (query row, head) outputs.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_31_amd as M
+import oracle.mla_oracle as O
+from mla_latent_kv_31_amd import runner
+from mla_workloads import gen
+from parity import TOL, OracleView, assert_abs_close, assert_rms_close, note
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LOG2E = 1.0 / math.log(2.0)
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------------------------------ toy
+@pytest.mark.parametrize("page_size,split", [(4, 4), (1, 1), (2, 2), (1, 3)])
+def test_toy_single_step_end_to_end(page_size, split):
+    """Toy fp32 step from hidden states: cache write, query projections, absorb, split-K decode,
+    combine and value projection all on the GPU; the oracle decompresses from the same h."""
+    note(f"toy page_size={page_size} split={split}")
+    t = gen.make_toy_inputs()
+    w = t["workload"]
+    d = runner.dims_for(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    h = dev(t["h"])
+    Lc = w.ctx
+    npages = -(-Lc // page_size)
+    pool = torch.full((npages + 1, page_size, w.d_c + w.d_r), float("nan"), device=DEV)
+    table = dev(np.arange(npages, dtype=np.int32)[None])
+    lens = dev(np.array([Lc], np.int32))
+    c = M.cache(pool, table, lens)
+    M.mla_kv_append(d, c, w.d_model, h, dev(t["w_dkv"]), dev(t["w_kr"]), dev(np.zeros(Lc, np.int32)),
+                    dev(np.arange(Lc, dtype=np.int32)), Lc, 0.0)
+    q_c = torch.empty((1, w.n_heads, w.d_k), device=DEV)
+    q_r = torch.empty((1, w.n_heads, w.d_r), device=DEV)
+    M.mla_project_query(d, w.d_model, w.d_cq, h[Lc - 1:Lc], dev(t["w_dq"]), dev(t["w_uq"]), dev(t["w_qr"]), 1, q_c, q_r)
+    q_hat = torch.empty((1, w.n_heads, w.d_c + w.d_r), device=DEV)
+    M.mla_absorb_query(d, q_c, q_r, dev(t["w_uk"]), dev(np.array([Lc - 1], np.int32)), 1, q_hat)
+    S = M.mla_decode_num_splits(Lc, split)
+    o_part = torch.empty((1, S, w.n_heads, w.d_c), device=DEV)
+    lse_part = torch.empty((1, S, w.n_heads), device=DEV)
+    M.mla_decode_partial(d, c, q_hat, Lc, split, o_part, lse_part)
+    z = torch.empty((1, w.n_heads, w.d_c), device=DEV)
+    lse = torch.empty((1, w.n_heads), device=DEV)
+    M.mla_combine(d, 1, S, o_part, lse_part, z, lse)
+    out = torch.empty((1, w.n_heads, w.d_v), device=DEV)
+    M.mla_out_proj(d, z, dev(t["w_uv"]), 1, out)
+    torch.cuda.synchronize()
+
+    hh = t["h"].astype(np.float64)
+    rows = O.cache_rows(O.kv_latent(hh, t["w_dkv"]), O.rope_key(hh, t["w_kr"], np.arange(Lc), w.rope_base))
+    _, qc, qr = O.query_parts(hh[Lc - 1], t["w_dq"], t["w_uq"], t["w_qr"])
+    ref = O.attention(qc, qr, Lc - 1, rows, t["w_uk"], t["w_uv"], w.d_c, base=w.rope_base)
+    tol = TOL["f32"]
+    got_rows = _np(pool)[np.arange(npages)].reshape(-1, w.d_c + w.d_r)[:Lc]
+    assert_rms_close(got_rows, rows, tol, "cache rows")
+    assert_rms_close(_np(q_c)[0], qc, tol, "q_c")
+    assert_rms_close(_np(q_r)[0], qr, tol, "q_r")
+    qh = O.absorbed_query(qc, qr, Lc - 1, t["w_uk"], w.rope_base) * (w.sm_scale * LOG2E)
+    assert_rms_close(_np(q_hat)[0], qh, tol, "q_hat")
+    zp, lp = O.chunk_partials(qc, qr, Lc - 1, rows, t["w_uk"], t["w_uv"], w.d_c, split, base=w.rope_base)
+    assert_rms_close(_np(o_part)[0], zp, tol, "o_part")
+    assert_abs_close(_np(lse_part)[0], lp, tol, "lse_part")
+    assert_rms_close(_np(z)[0], ref["z"], tol, "z")
+    assert_abs_close(_np(lse)[0], ref["lse"], tol, "lse")
+    assert_rms_close(_np(out)[0], ref["o"], tol, "o")
+
+
+# ------------------------------------------------------------------------------------------ V3 decode
+@pytest.fixture(scope="module")
+def inp_b1():
+    return gen.make_decode_inputs(gen.WORKLOADS["v3_b1_ctx4k"])
+
+
+def _check_full_sequence(step, view, b, tol, flags_note=""):
+    ref = view.decode(b)
+    assert_rms_close(_np(step.z)[b], ref["z"], tol, f"z seq {b} {flags_note}")
+    assert_abs_close(_np(step.lse)[b], ref["lse"], tol, f"lse seq {b} {flags_note}")
+    assert_rms_close(_np(step.out)[b], ref["o"], tol, f"o seq {b} {flags_note}")
+
+
+@pytest.mark.parametrize("flags", [0, M.MLA_FLAG_FORCE_GENERIC])
+def test_v3_b1_ctx4k_all_heads(inp_b1, flags):
+    w = inp_b1["workload"]
+    note(f"v3_b1_ctx4k flags={flags} split={w.split_tokens}")
+    st = runner.DecodeStep(inp_b1, w.split_tokens, DEV, flags=flags)
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp_b1)
+    tol = TOL["bf16"]
+    assert_rms_close(_np(st.q_hat)[0], view.q_hat(0) * (w.sm_scale * LOG2E), tol, "q_hat")
+    _check_full_sequence(st, view, 0, tol, f"flags={flags}")
+    # split partials of the first, a middle and the last chunk
+    for i in (0, st.S // 2, st.S - 1):
+        r = view.decode(0, key_range=(i * st.split_tokens, (i + 1) * st.split_tokens))
+        assert_rms_close(_np(st.o_part)[0, i], r["z"], tol, f"o_part chunk {i}")
+        assert_abs_close(_np(st.lse_part)[0, i], r["lse"], tol, f"lse_part chunk {i}")
+
+
+@pytest.fixture(scope="module")
+def inp_ragged():
+    return gen.make_decode_inputs(gen.WORKLOADS["v3_b64_ragged_paged"])
+
+
+def test_v3_b64_ragged_paged_sampled(inp_ragged):
+    w = inp_ragged["workload"]
+    note(f"v3_b64_ragged_paged split={w.split_tokens} total_tokens={int(inp_ragged['lens'].sum())}")
+    st = runner.DecodeStep(inp_ragged, w.split_tokens, DEV)
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp_ragged)
+    lens = inp_ragged["lens"]
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    heads = [0, 77, 127]
+    tol = TOL["bf16"]
+    for b in seqs:
+        ref = view.decode(b, heads=heads)
+        assert_rms_close(_np(st.z)[b, heads], ref["z"][heads], tol, f"z seq {b}")
+        assert_abs_close(_np(st.lse)[b, heads], ref["lse"][heads], tol, f"lse seq {b}")
+        assert_rms_close(_np(st.out)[b, heads], ref["o"][heads], tol, f"o seq {b}")
+    # any-size properties on every output: finite, and z inside the convex hull bound of |c|
+    assert np.isfinite(_np(st.out)).all() and np.isfinite(_np(st.lse)).all()
+
+
+@pytest.fixture(scope="module")
+def inp_long():
+    return gen.make_decode_inputs(gen.WORKLOADS["v3_b4_ctx128k"])
+
+
+def test_v3_b4_ctx128k_sampled(inp_long):
+    w = inp_long["workload"]
+    note(f"v3_b4_ctx128k split={w.split_tokens}")
+    st = runner.DecodeStep(inp_long, w.split_tokens, DEV)
+    assert st.S >= 256
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp_long)
+    tol = TOL["bf16"]
+    for b, h in ((0, 3), (3, 126)):
+        ref = view.decode(b, heads=[h])
+        assert_rms_close(_np(st.z)[b, h], ref["z"][h], tol, f"z ({b},{h})")
+        assert_abs_close(_np(st.lse)[b, h], ref["lse"][h], tol, f"lse ({b},{h})")
+        assert_rms_close(_np(st.out)[b, h], ref["o"][h], tol, f"o ({b},{h})")
+    for i in (0, 1, 128, st.S - 1):
+        r = view.decode(1, heads=[5], key_range=(i * st.split_tokens, (i + 1) * st.split_tokens))
+        assert_rms_close(_np(st.o_part)[1, i, 5], r["z"][5], tol, f"o_part chunk {i}")
+        assert_abs_close(_np(st.lse_part)[1, i, 5], r["lse"][5], tol, f"lse_part chunk {i}")
+
+
+# ------------------------------------------------------------------------------------------ prefill
+@pytest.fixture(scope="module")
+def inp_prefill():
+    return gen.make_prefill_inputs(gen.WORKLOADS["v3_prefill_b2"])
+
+
+@pytest.mark.parametrize("flags", [0, M.MLA_FLAG_FORCE_GENERIC])
+def test_v3_prefill_sampled(inp_prefill, flags):
+    note(f"v3_prefill_b2 flags={flags}")
+    st = runner.PrefillStep(inp_prefill, DEV, flags=flags)
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp_prefill)
+    tol = TOL["bf16"]
+    heads = [0, 64, 127]
+    for b in (0, 1):
+        for i in (0, 1, 63, 64, 255, 510, 511):
+            ref = view.prefill_row(b, i, heads)
+            assert_rms_close(_np(st.z)[b, i, heads], ref["z"][heads], tol, f"z ({b},{i})")
+            assert_abs_close(_np(st.lse)[b, i, heads], ref["lse"][heads], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i, heads], ref["o"][heads], tol, f"o ({b},{i})")
+
+
+# ------------------------------------------------------------------------------------------ small V3 shapes
+def _small(dtype, lens, seed=11, random_pages=True, H=128):
+    w = gen.Workload(name="small", seed=seed, kind="decode", batch=len(lens), n_heads=H, dtype=dtype,
+                     random_pages=random_pages)
+    return gen.make_decode_inputs(w, lens=np.array(lens, np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("split", [64, 192, 4096])
+def test_v3_small_ragged_all_heads(dtype, split):
+    lens = [1, 63, 64, 65, 300, 1000]
+    note(f"small ragged dtype={dtype} split={split}")
+    inp = _small(dtype, lens)
+    st = runner.DecodeStep(inp, split, DEV)
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp)
+    for b in range(len(lens)):
+        _check_full_sequence(st, view, b, TOL[dtype], f"{dtype} split={split}")
+
+
+def test_empty_sequence_and_spare_chunks():
+    """A zero-length sequence yields z = 0, o = 0, lse = -inf; a max_len well above every length
+    adds empty chunks that must not change the others."""
+    lens = [0, 130, 5]
+    note("empty sequence + spare chunks")
+    inp = _small("bf16", lens, seed=12)
+    inp["lens"] = np.array(lens, np.int32)
+    st = runner.DecodeStep(inp, 64, DEV, max_len=inp["page_table"].shape[1] * 64)
+    st.run()
+    torch.cuda.synchronize()
+    z, lse, out = _np(st.z), _np(st.lse), _np(st.out)
+    assert np.all(z[0] == 0) and np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+    assert np.all(_np(st.lse_part)[0] == -np.inf) and np.all(_np(st.o_part)[0] == 0)
+    view = OracleView(inp)
+    for b in (1, 2):
+        _check_full_sequence(st, view, b, TOL["bf16"], "spare chunks")
