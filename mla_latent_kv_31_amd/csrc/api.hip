@@ -91,10 +91,11 @@ int32_t mla_decode_num_splits(int32_t max_len, int32_t split_tokens) {
 }
 
 int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32_t split_tokens) {
-  (void)dims;
-  (void)cache;
-  (void)split_tokens;
-  return 0;
+  Dims d;
+  Cache c;
+  if (check_dims(dims, &d) != MLA_OK || check_cache(cache, &c) != MLA_OK) return 0;
+  if (dims->flags & MLA_FLAG_FORCE_GENERIC) return 0;
+  return decode_mfma_supported(d, c, split_tokens) ? 1 : 0;
 }
 
 int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache) {
@@ -130,6 +131,8 @@ mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, cons
   if (max_len < 0 || int64_t(max_len) > int64_t(c.max_pages) * c.page_size) return MLA_ERR_SHAPE;
   const int S = mla_decode_num_splits(max_len, split_tokens);
   if (c.batch == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && decode_mfma_supported(d, c, split_tokens))
+    return hip_status(launch_decode_mfma(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
   return hip_status(launch_decode_generic(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
 }
 

@@ -28,6 +28,11 @@ constexpr int kGenericMaxDc = 1024;   // latent width handled by the generic dec
 constexpr int kGenericMaxRow = 2048;  // d_c + d_r
 constexpr int kGenericMaxDk = 1024;
 
+// ---- bf16 MFMA decode for the DeepSeek-V3 shape (128 heads, d_c 512, d_r 64, 64-token tiles)
+bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens);
+hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
+                              float* o_part, float* lse_part, hipStream_t s);
+
 hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
                                  const int32_t* pos, int rows, void* q_hat, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const Cache& c, const void* q_hat, int n_splits,
