@@ -104,7 +104,8 @@ int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache);
  * z = a.C, the rotary part is never summed):
  *   o_part[b,i,h,:] = sum_t softmax_t(s) c_t  (normalised within the chunk)
  *   lse_part[b,i,h] = ln sum_t exp(s_t)        with s_t = q_hat . row_t / log2(e)
- * An empty chunk writes o_part = 0 and lse_part = -inf.
+ * An empty chunk writes lse_part = -inf and may leave its o_part row untouched: the combine gives
+ * it zero weight and never reads it.
  *   q_hat    device dtype [batch, H, d_c + d_r]   (as written by mla_absorb_query)
  *   max_len  host bound >= every seq_lens[b]; sets S = mla_decode_num_splits(max_len, split_tokens)
  *   split_tokens  > 0 and a multiple of cache->page_size

@@ -115,6 +115,8 @@ mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q
   MLA_TRY(ptr_ok(pos));
   MLA_TRY(ptr_ok(q_hat));
   if (rows == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && proj_mfma_supported(d))
+    return hip_status(launch_absorb_mfma(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
   return hip_status(launch_absorb_generic(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
 }
 
@@ -147,6 +149,8 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, co
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
   if (batch == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_splits))
+    return hip_status(launch_combine_fast(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
   return hip_status(launch_combine_generic(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
 }
 
@@ -160,6 +164,8 @@ mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, 
   MLA_TRY(ptr_ok(w_uv));
   MLA_TRY(ptr_ok(out));
   if (rows == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && proj_mfma_supported(d))
+    return hip_status(launch_out_proj_mfma(d, z, w_uv, rows, out, (hipStream_t)stream));
   return hip_status(launch_out_proj_generic(d, z, w_uv, rows, out, (hipStream_t)stream));
 }
 

@@ -1,0 +1,78 @@
+// Log-sum-exp merge of split-K partials for latent widths up to 512 (a multiple of 8):
+//   LSE = ln sum_i exp(lse_i),  z = sum_i exp(lse_i - LSE) o_i
+// over any split equal to the single-pass softmax of the scores ([ase] Fig. 2).  One wave per
+// (sequence, head): lanes first reduce the chunk maxima and weights (kept in LDS), then each lane
+// accumulates eight latent columns over the chunks with 16-byte loads; chunks of weight zero
+// (empty or negligible) are never read.
+
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+constexpr int kCombineMaxSplits = 2048;
+
+// grid (H / 4, batch); wave w handles head 4*blockIdx.x + w.
+__global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part, float* __restrict__ z,
+                                                      float* __restrict__ lse_out) {
+  __shared__ float wts[4][kCombineMaxSplits];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = 4 * blockIdx.x + wave, b = blockIdx.y;
+  if (h >= H) return;  // whole wave leaves; no block-wide barrier follows
+  const float* lp = lse_part + size_t(b) * S * H + h;
+  float mx = -INFINITY;
+  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lp[size_t(s) * H]);
+  mx = wave_max(mx);
+  float* zo = z + (size_t(b) * H + h) * dc;
+  if (mx == -INFINITY) {
+    for (int c = lane * 4; c < dc; c += 256) *reinterpret_cast<float4*>(zo + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane == 0 && lse_out) lse_out[size_t(b) * H + h] = -INFINITY;
+    return;
+  }
+  float tot = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float w = expf(lp[size_t(s) * H] - mx);
+    wts[wave][s] = w;
+    tot += w;
+  }
+  tot = wave_sum(tot);
+  const float inv = 1.f / tot;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+  const int c0 = 8 * lane;
+  if (c0 < dc) {
+    const float* op = o_part + (size_t(b) * S * H + h) * dc + c0;
+    const size_t stride = size_t(H) * dc;
+    for (int s = 0; s < S; ++s) {
+      const float w = wts[wave][s] * inv;
+      if (w == 0.f) continue;  // empty chunk (its partial may be unwritten) or negligible weight
+      const float4 x0 = *reinterpret_cast<const float4*>(op + s * stride);
+      const float4 x1 = *reinterpret_cast<const float4*>(op + s * stride + 4);
+      a0.x = fmaf(w, x0.x, a0.x); a0.y = fmaf(w, x0.y, a0.y); a0.z = fmaf(w, x0.z, a0.z); a0.w = fmaf(w, x0.w, a0.w);
+      a1.x = fmaf(w, x1.x, a1.x); a1.y = fmaf(w, x1.y, a1.y); a1.z = fmaf(w, x1.z, a1.z); a1.w = fmaf(w, x1.w, a1.w);
+    }
+    *reinterpret_cast<float4*>(zo + c0) = a0;
+    *reinterpret_cast<float4*>(zo + c0 + 4) = a1;
+  }
+  if (lane == 0 && lse_out) lse_out[size_t(b) * H + h] = mx + logf(tot);
+}
+
+}  // namespace
+
+bool combine_fast_supported(const Dims& d, int n_splits) {
+  return d.dc % 8 == 0 && d.dc <= 512 && n_splits <= kCombineMaxSplits;
+}
+
+hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
+                               float* z, float* lse, hipStream_t s) {
+  combine_kernel<<<dim3((d.H + 3) / 4, batch), 256, 0, s>>>(d.H, d.dc, n_splits, o_part, lse_part, z, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

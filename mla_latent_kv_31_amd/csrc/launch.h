@@ -33,6 +33,16 @@ bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens);
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
                               float* o_part, float* lse_part, hipStream_t s);
 
+// ---- bf16 MFMA per-head projections (d_c 512, d_k = d_v = 128) and the vectorised combine
+bool proj_mfma_supported(const Dims& d);
+hipError_t launch_absorb_mfma(const Dims& d, const void* q_c, const void* q_r, const void* w_uk, const int32_t* pos,
+                              int rows, void* q_hat, hipStream_t s);
+hipError_t launch_out_proj_mfma(const Dims& d, const float* z, const void* w_uv, int rows, float* out,
+                                hipStream_t s);
+bool combine_fast_supported(const Dims& d, int n_splits);
+hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
+                               float* z, float* lse, hipStream_t s);
+
 hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
                                  const int32_t* pos, int rows, void* q_hat, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const Cache& c, const void* q_hat, int n_splits,

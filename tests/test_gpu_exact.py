@@ -47,6 +47,13 @@ def _run_partial(inp, split, q_hat_np=None, flags=0, max_len=None):
 PATHS = [0, M.MLA_FLAG_FORCE_GENERIC]
 
 
+def _masked_parts(st):
+    """Split partials of the non-empty chunks (an empty chunk's o_part row is left untouched)."""
+    o = _np(st.o_part).copy()
+    o[~np.isfinite(_np(st.lse_part))] = 0.0
+    return o
+
+
 @pytest.mark.parametrize("flags", PATHS)
 @pytest.mark.parametrize("split", [64, 128, 512])
 def test_count(split, flags):
@@ -59,9 +66,8 @@ def test_count(split, flags):
     for b, L in enumerate(lens):
         for i in range(st.S):
             cnt = max(0, min(L, (i + 1) * split) - i * split)
-            if cnt == 0:
+            if cnt == 0:  # empty chunk: lse = -inf (its o_part is never read)
                 assert np.all(lse_p[b, i] == -np.inf), (b, i)
-                assert np.all(o_p[b, i] == 0.0), (b, i)
                 continue
             e = np.exp(lse_p[b, i].astype(np.float64))
             assert np.all(np.rint(e) == cnt), (b, i, cnt, e[:4])
@@ -118,7 +124,7 @@ def test_poison_bitwise(flags):
         st = _run_partial(inp, 128, flags=flags)
         st.out_proj()
         torch.cuda.synchronize()
-        outs.append([_np(x).copy() for x in (st.o_part, st.lse_part, st.z, st.lse, st.out)])
+        outs.append([_masked_parts(st)] + [_np(x).copy() for x in (st.lse_part, st.z, st.lse, st.out)])
     for other in outs[1:]:
         for a, b in zip(outs[0], other):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
@@ -132,11 +138,11 @@ def test_page_permutation_bitwise_and_determinism(flags):
     for rp in (False, True):
         inp = gen.make_decode_inputs(_w(len(lens), random_pages=rp), lens=lens, fill="zero", random_pages=rp)
         st = _run_partial(inp, 256, flags=flags)
-        res.append([_np(x).copy() for x in (st.o_part, st.lse_part, st.z, st.lse)])
+        res.append([_masked_parts(st)] + [_np(x).copy() for x in (st.lse_part, st.z, st.lse)])
         st.attend()
         st.combine()
         torch.cuda.synchronize()
-        again = [_np(x) for x in (st.o_part, st.lse_part, st.z, st.lse)]
+        again = [_masked_parts(st)] + [_np(x) for x in (st.lse_part, st.z, st.lse)]
         for a, b in zip(res[-1], again):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "re-run differs"
     for a, b in zip(res[0], res[1]):
