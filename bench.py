@@ -1,16 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark: MLA decode over a latent cache on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--split-tokens T]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--split-tokens T | --units N]
 
 A step is one pass of the whole decode hot path over one batch of synthetic
 DeepSeek-V3-shaped input already resident in HBM:
-    mla_absorb_query -> mla_decode_partial -> mla_combine -> mla_out_proj
+    mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced -> mla_out_proj
+by default (work-balanced split over the compute units), or with --split-tokens T
+the fixed-chunk pair mla_decode_partial -> mla_combine.
 W untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation.  Prints one JSON line.
 
 value = cache GB/s = (sum over sequences of cached tokens x 1,152 B) / time per step.
-The roofline object covers the dominant kernel (mla_decode_partial): its
+The roofline object covers the dominant kernel (the split-K decode): its
 algorithmic bytes per launch over its average duration, timed with HIP events
 on the stream it runs on.  cpu_baseline times the fp64 oracle on a bounded
 sample of the same workload on the host cores.
@@ -32,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 DEFAULT_WORKLOAD = "v3_b64_ragged_paged"
-DECODE_SOURCES = ("mla_latent_kv_31_amd/csrc/decode_mfma.hip", "mla_latent_kv_31_amd/csrc/generic.hip")
+DECODE_SOURCES = ("mla_latent_kv_31_amd/csrc/decode_mfma.hip", "mla_latent_kv_31_amd/csrc/schedule.h",
+                  "mla_latent_kv_31_amd/csrc/common.h")
 
 
 def _kernel_sha() -> str:
@@ -105,7 +108,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--split-tokens", type=int, default=None)
+    ap.add_argument("--split-tokens", type=int, default=None,
+                    help="fixed split-K chunks of this many tokens instead of the balanced split")
+    ap.add_argument("--units", type=int, default=None, help="units of the balanced split (default: one per CU)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -126,10 +131,13 @@ def main() -> int:
     if w.kind != "decode":
         print(f"workload {w.name} is not a decode workload", file=sys.stderr)
         return 2
-    split = args.split_tokens or w.split_tokens
     inp = gen.make_decode_inputs(w)
     dev = torch.device("cuda:0")
-    st = runner.DecodeStep(inp, split, dev)
+    if args.split_tokens:
+        st = runner.DecodeStep(inp, args.split_tokens, dev)
+    else:
+        n_units = args.units or runner.balanced_units(inp["lens"], runner.compute_units(dev))
+        st = runner.DecodeStep(inp, 0, dev, n_units=n_units)
     lens = inp["lens"].astype(np.int64)
     total_tokens = int(lens.sum())
     row_bytes = (w.d_c + w.d_r) * 2
@@ -178,8 +186,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.n_heads, "d_c": w.d_c, "d_r": w.d_r,
-                   "d_k": w.d_k, "d_v": w.d_v, "page_size": w.page_size, "split_tokens": split,
-                   "n_splits": st.S, "cache_tokens": total_tokens, "seed": w.seed,
+                   "d_k": w.d_k, "d_v": w.d_v, "page_size": w.page_size,
+                   "split": f"fixed {st.split_tokens}" if st.n_units is None else f"balanced {st.n_units} units",
+                   "partials": st.S * (st.B if st.n_units is None else 1), "cache_tokens": total_tokens, "seed": w.seed,
                    "decode_kernel": "mfma" if st.uses_mfma() else "generic"},
         "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "cache_tokens_per_s": round(total_tokens / (ms_step * 1e-3), 1),

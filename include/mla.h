@@ -93,7 +93,8 @@ mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q
 /* Number of split-K chunks per sequence: ceil(max_len / split_tokens), at least 1. */
 int32_t mla_decode_num_splits(int32_t max_len, int32_t split_tokens);
 
-/* Nonzero when mla_decode_partial / mla_prefill_chunk take the MFMA kernels for these arguments. */
+/* Nonzero when mla_decode_partial / mla_prefill_chunk take the MFMA kernels for these arguments
+ * (split_tokens == 0 asks about mla_decode_partial_balanced). */
 int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32_t split_tokens);
 int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache);
 
@@ -124,6 +125,44 @@ mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, cons
  *   lse      device float [batch, H] or NULL   (output)                                          */
 mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const float* o_part,
                        const float* lse_part, float* z, float* lse, void* stream);
+
+/* Work-balanced split-K ([ase] Fig. 2 softmax over all cached positions, evaluated piecewise and
+ * merged as in mla_combine).  Fixed-size chunks leave most of the GPU idle on ragged batches; this
+ * variant splits the whole batch into n_units pieces of equal cost, so one launch of n_units
+ * workgroups (one per compute unit) finishes together.  The split is a pure function of seq_lens:
+ *   len_b   = min(max(seq_lens[b], 0), max_pages * page_size)
+ *   tiles_b = ceil(len_b / MLA_BALANCED_TILE)
+ *   cost_b  = tiles_b > 0 ? tiles_b + MLA_BALANCED_SEG_COST : 0,   C_b = cost_0 + ... + cost_{b-1}
+ *   q       = ceil(C_batch / n_units)
+ * Unit w owns cost positions [w*q, (w+1)*q); sequence b's tiles sit at positions
+ * C_b + MLA_BALANCED_SEG_COST + k, k = 0 .. tiles_b-1 (the leading positions price the fixed cost
+ * of a segment).  Segment (w, b) = the tiles of b in unit w, i.e. tokens
+ * [MLA_BALANCED_TILE*k0, min(MLA_BALANCED_TILE*k1, len_b)); when non-empty its partial goes to
+ * slot w + b, distinct for distinct non-empty segments.  Slots of empty segments are not written. */
+#define MLA_BALANCED_TILE 32
+#define MLA_BALANCED_SEG_COST 8
+#define MLA_BALANCED_MAX_UNITS 2048
+
+/* Number of partial slots of the balanced split: n_units + batch - 1 (-1 on bad arguments). */
+int32_t mla_balanced_num_slots(int32_t batch, int32_t n_units);
+
+/* Balanced split-K decode: writes, for every non-empty segment (w, b) and head h, the same
+ * chunk-local pair as mla_decode_partial over the segment's tokens:
+ *   o_part[w+b,h,:]  (normalised),  lse_part[w+b,h]  (natural log)
+ *   n_units  1 .. MLA_BALANCED_MAX_UNITS
+ *   o_part   device float [mla_balanced_num_slots(batch, n_units), H, d_c]
+ *   lse_part device float [mla_balanced_num_slots(batch, n_units), H]
+ * MLA_ERR_UNSUPPORTED when batch * (max_pages*page_size / MLA_BALANCED_TILE + 9) >= 2^31 - 2^12. */
+mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                       int32_t n_units, float* o_part, float* lse_part, void* stream);
+
+/* Merge of the balanced partials: for every sequence, the log-sum-exp merge of mla_combine over
+ * the slots of its non-empty segments (none: z = 0, lse = -inf).  cache supplies seq_lens, batch,
+ * page_size and max_pages (pool and page_table are not read but must be valid pointers).
+ *   z   device float [batch, H, d_c]   (output)
+ *   lse device float [batch, H] or NULL (output)                                                  */
+mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                const float* o_part, const float* lse_part, float* z, float* lse, void* stream);
 
 /* Value up-projection applied once after the weighted sum ([ase] "Value 투영을 가중합 뒤로
  * 옮기기", Fig. 4 equation; [huny] section 2, value absorption):

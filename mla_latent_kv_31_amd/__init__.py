@@ -7,6 +7,9 @@ the names and argument order of the C entry points and only marshal arguments.
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    MLA_BALANCED_MAX_UNITS,
+    MLA_BALANCED_SEG_COST,
+    MLA_BALANCED_TILE,
     MLA_BF16,
     MLA_ERR_ALIGN,
     MLA_ERR_DTYPE,
@@ -24,9 +27,12 @@ from ._lib import (  # noqa: F401
     dims,
     library,
     mla_absorb_query,
+    mla_balanced_num_slots,
     mla_combine,
+    mla_combine_balanced,
     mla_decode_num_splits,
     mla_decode_partial,
+    mla_decode_partial_balanced,
     mla_decode_uses_mfma,
     mla_kv_append,
     mla_out_proj,

@@ -26,6 +26,11 @@ MLA_F32 = 0
 MLA_BF16 = 1
 MLA_FLAG_FORCE_GENERIC = 1
 
+# Balanced split-K constants (include/mla.h)
+MLA_BALANCED_TILE = 32
+MLA_BALANCED_SEG_COST = 8
+MLA_BALANCED_MAX_UNITS = 2048
+
 
 class MlaDims(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_c", ctypes.c_int32), ("d_r", ctypes.c_int32),
@@ -58,6 +63,9 @@ _SIGNATURES = {
     "mla_prefill_uses_mfma": (_I32, [_PD, _PC]),
     "mla_decode_partial": (_I32, [_PD, _PC, _VP, _I32, _I32, _VP, _VP, _VP]),
     "mla_combine": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "mla_balanced_num_slots": (_I32, [_I32, _I32]),
+    "mla_decode_partial_balanced": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP]),
+    "mla_combine_balanced": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP]),
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
@@ -158,6 +166,24 @@ def mla_decode_partial(d: MlaDims, c: MlaCache, q_hat, max_len: int, split_token
 def mla_combine(d: MlaDims, batch: int, n_splits: int, o_part, lse_part, z, lse=None, stream=None) -> None:
     _check(library().mla_combine(ctypes.byref(d), batch, n_splits, _addr(o_part), _addr(lse_part), _addr(z),
                                  _addr(lse), _stream(stream)), "mla_combine")
+
+
+def mla_balanced_num_slots(batch: int, n_units: int) -> int:
+    return library().mla_balanced_num_slots(batch, n_units)
+
+
+def mla_decode_partial_balanced(d: MlaDims, c: MlaCache, q_hat, n_units: int, o_part, lse_part,
+                                stream=None) -> None:
+    _check(library().mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), _addr(q_hat), n_units,
+                                                 _addr(o_part), _addr(lse_part), _stream(stream)),
+           "mla_decode_partial_balanced")
+
+
+def mla_combine_balanced(d: MlaDims, c: MlaCache, n_units: int, o_part, lse_part, z, lse=None,
+                         stream=None) -> None:
+    _check(library().mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n_units, _addr(o_part),
+                                          _addr(lse_part), _addr(z), _addr(lse), _stream(stream)),
+           "mla_combine_balanced")
 
 
 def mla_out_proj(d: MlaDims, z, w_uv, rows: int, out, stream=None) -> None:

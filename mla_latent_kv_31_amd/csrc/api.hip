@@ -51,6 +51,15 @@ mla_status check_cache(const mla_cache* cache, Cache* out) {
   return MLA_OK;
 }
 
+// The balanced split counts costs in int32 on the device: keep the total well inside its range.
+mla_status check_balanced(const Cache& c, int n_units) {
+  if (n_units < 1) return MLA_ERR_SHAPE;
+  if (n_units > MLA_BALANCED_MAX_UNITS) return MLA_ERR_UNSUPPORTED;
+  const int64_t per_seq = int64_t(c.max_pages) * c.page_size / MLA_BALANCED_TILE + 1 + MLA_BALANCED_SEG_COST;
+  if (int64_t(c.batch) * per_seq >= (int64_t(1) << 31) - (int64_t(1) << 12)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 mla_status ptr_ok(const void* p) {
   if (!p) return MLA_ERR_NULL;
   return aligned16(p) ? MLA_OK : MLA_ERR_ALIGN;
@@ -152,6 +161,44 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, co
   if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_splits))
     return hip_status(launch_combine_fast(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
   return hip_status(launch_combine_generic(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
+}
+
+int32_t mla_balanced_num_slots(int32_t batch, int32_t n_units) {
+  if (batch < 0 || n_units < 1 || n_units > MLA_BALANCED_MAX_UNITS) return -1;
+  return batch == 0 ? 0 : n_units + batch - 1;
+}
+
+mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                       int32_t n_units, float* o_part, float* lse_part, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  MLA_TRY(check_balanced(c, n_units));
+  MLA_TRY(ptr_ok(q_hat));
+  MLA_TRY(ptr_ok(o_part));
+  MLA_TRY(ptr_ok(lse_part));
+  if (c.batch == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && decode_mfma_supported(d, c, 0))
+    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream));
+  return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream));
+}
+
+mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units, const float* o_part,
+                                const float* lse_part, float* z, float* lse, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  MLA_TRY(check_balanced(c, n_units));
+  MLA_TRY(ptr_ok(o_part));
+  MLA_TRY(ptr_ok(lse_part));
+  MLA_TRY(ptr_ok(z));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (c.batch == 0) return MLA_OK;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_units))
+    return hip_status(launch_combine_fast_balanced(d, c, n_units, o_part, lse_part, z, lse, (hipStream_t)stream));
+  return hip_status(launch_combine_generic_balanced(d, c, n_units, o_part, lse_part, z, lse, (hipStream_t)stream));
 }
 
 mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,

@@ -3,29 +3,48 @@
 // over any split equal to the single-pass softmax of the scores ([ase] Fig. 2).  One wave per
 // (sequence, head): lanes first reduce the chunk maxima and weights (kept in LDS), then each lane
 // accumulates eight latent columns over the chunks with 16-byte loads; chunks of weight zero
-// (empty or negligible) are never read.
+// (empty or negligible) are never read.  The balanced split (schedule.h) merges the slots of each
+// sequence's segments.
 
 #include <math.h>
 
 #include "common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mla {
 namespace {
 
 constexpr int kCombineMaxSplits = 2048;
 
-// grid (H / 4, batch); wave w handles head 4*blockIdx.x + w.
-__global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, const float* __restrict__ o_part,
+// grid (H / 4, batch); wave w handles head 4*blockIdx.x + w.  The partials of sequence b are the
+// `count` consecutive slots from `base`: the S chunks b*S .. b*S+S-1 of the fixed split, or the
+// slots of b's segments in the balanced split (recomputed from seq_lens, see schedule.h).
+template <bool kBalanced>
+__global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, const int32_t* __restrict__ seq_lens,
+                                                      int batch, int cap, const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, float* __restrict__ z,
                                                       float* __restrict__ lse_out) {
   __shared__ float wts[4][kCombineMaxSplits];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = 4 * blockIdx.x + wave, b = blockIdx.y;
   if (h >= H) return;  // whole wave leaves; no block-wide barrier follows
-  const float* lp = lse_part + size_t(b) * S * H + h;
+  int base = b * S, count = S;
+  if constexpr (kBalanced) {
+    int cb, total;
+    sched_prefix(seq_lens, batch, cap, b, cb, total);
+    const int tiles = sched_tiles(sched_len(seq_lens[b], cap));
+    count = 0;
+    if (tiles > 0) {
+      int w0, w1;
+      sched_units(cb, tiles, sched_quota(total, S), w0, w1);
+      base = w0 + b;
+      count = w1 - w0 + 1;
+    }
+  }
+  const float* lp = lse_part + size_t(base) * H + h;
   float mx = -INFINITY;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lp[size_t(s) * H]);
+  for (int s = lane; s < count; s += 64) mx = fmaxf(mx, lp[size_t(s) * H]);
   mx = wave_max(mx);
   float* zo = z + (size_t(b) * H + h) * dc;
   if (mx == -INFINITY) {
@@ -34,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
     return;
   }
   float tot = 0.f;
-  for (int s = lane; s < S; s += 64) {
+  for (int s = lane; s < count; s += 64) {
     const float w = expf(lp[size_t(s) * H] - mx);
     wts[wave][s] = w;
     tot += w;
@@ -47,9 +66,9 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
   float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
   const int c0 = 8 * lane;
   if (c0 < dc) {
-    const float* op = o_part + (size_t(b) * S * H + h) * dc + c0;
+    const float* op = o_part + (size_t(base) * H + h) * dc + c0;
     const size_t stride = size_t(H) * dc;
-    for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < count; ++s) {
       const float w = wts[wave][s] * inv;
       if (w == 0.f) continue;  // empty chunk (its partial may be unwritten) or negligible weight
       const float4 x0 = *reinterpret_cast<const float4*>(op + s * stride);
@@ -71,7 +90,15 @@ bool combine_fast_supported(const Dims& d, int n_splits) {
 
 hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                float* z, float* lse, hipStream_t s) {
-  combine_kernel<<<dim3((d.H + 3) / 4, batch), 256, 0, s>>>(d.H, d.dc, n_splits, o_part, lse_part, z, lse);
+  combine_kernel<false><<<dim3((d.H + 3) / 4, batch), 256, 0, s>>>(d.H, d.dc, n_splits, nullptr, batch, 0, o_part,
+                                                                   lse_part, z, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+                                        const float* lse_part, float* z, float* lse, hipStream_t s) {
+  combine_kernel<true><<<dim3((d.H + 3) / 4, c.batch), 256, 0, s>>>(
+      d.H, d.dc, n_units, c.seq_lens, c.batch, c.max_pages * c.page_size, o_part, lse_part, z, lse);
   return hipGetLastError();
 }
 

@@ -46,6 +46,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mla {
 namespace {
@@ -112,39 +113,37 @@ __device__ __forceinline__ void dma16_if(uint32_t go, uint32_t lds_dst, uint32_t
                : "memory", "scc");
 }
 
+// Page ids of 64 consecutive pages of a sequence's table, one per lane, loaded and waited for in
+// one asm block.  Tile addresses are then taken with v_readlane: a compiler-visible load here
+// would leave a pending-load state at the loop joins and make the compiler drain every tile
+// transfer in flight before the next use.  Lanes past the last page read the final table entry.
+__device__ __forceinline__ int load_page_window(const int32_t* row, int first, int count, int max_pages, int lane) {
+  const uint32_t off = 4u * uint32_t(min(first + lane, max_pages - 1));
+  int v;
+  asm volatile("global_load_dword %0, %1, %2\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(off), "s"(row) : "memory");
+  return lane < count ? v : 0;
+}
+
+// One workgroup runs a list of segments (sequence, token range, partial slot): one chunk of the
+// fixed split (grid = chunks x sequences), or every segment of one unit of the balanced split
+// (grid = units; see schedule.h).
+template <bool kBalanced>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __restrict__ page_table,
-                        const int32_t* __restrict__ seq_lens, int max_pages, int page_size,
+                        const int32_t* __restrict__ seq_lens, int batch, int max_pages, int page_size,
                         int tiles_per_page_log2, const uint16_t* __restrict__ q_hat, int n_splits,
                         int split_tokens, float* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kNBuf * kTileB + kH * kRopeB];  // 160 KiB
   lds_u8* const lbase = (lds_u8*)smem;
 
-  const int chunk = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hi = lane >> 5;
   const int head = wave * 32 + (lane & 31);
-  const int len = min(seq_lens[b], max_pages * page_size);  // never index past the page table
-  const int t0 = chunk * split_tokens;
-  const int t1 = min(t0 + split_tokens, len);
-  const size_t orow = (size_t(b) * n_splits + chunk) * kH + head;
+  const int cap = max_pages * page_size;  // never index past the page table
 
-  if (t0 >= t1) {  // empty chunk: lse = -inf; its o_part is never read by the combine
-    if (hi == 0) lse_part[orow] = -INFINITY;
-    return;
-  }
-  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-
-  // Page ids of this chunk, one per lane (a chunk spans at most 64 pages).  Tile addresses are
-  // then read with v_readlane: a scalar load of the page table inside the loop would share the
-  // LDS counter and, completing out of order, force full waits on every in-flight LDS read.
-  const int pg0 = t0 / page_size;
-  const int npg = (t1 - t0 + page_size - 1) / page_size;
-  const int my_page = lane < npg ? page_table[size_t(b) * max_pages + pg0 + lane] : 0;
-
-  // ---- tile transfers.  Latent row n = 4x + wave (x < 8) is one 1 KiB transfer; rotary rows
-  // 8*wave .. 8*wave+7 are this wave's ninth.  Lane L writes LDS chunk L of the transfer; the
-  // global chunk it reads is the one that the XOR swizzle places there.
+  // ---- per-lane constants of the tile transfers.  Latent row n = 4x + wave (x < 8) is one 1 KiB
+  // transfer; rotary rows 8*wave .. 8*wave+7 are this wave's ninth.  Lane L writes LDS chunk L of
+  // the transfer; the global chunk it reads is the one that the XOR swizzle places there.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto lat_off = [&](int x) {  // the swizzle of row n = 4x + wave depends on n & 15
     return uint32_t(16 * ((lane & ~15) | ((lane ^ lat_swz(4 * (x & 3) + wave_u)) & 15)));
@@ -153,50 +152,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     return uint32_t((lane >> 3) * kRowB + kLatB + 16 * ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)));
   };
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lbase));
-  auto tile_src = [&](int k) {
-    const int pg = __builtin_amdgcn_readlane(my_page, k >> tiles_per_page_log2);
-    const int in_page = (k & ((1 << tiles_per_page_log2) - 1)) * kTile;
-    return reinterpret_cast<const unsigned char*>(pool + (size_t(pg) * page_size + in_page) * kW);
-  };
-  auto dma_one = [&](uint32_t go, const unsigned char* g, uint32_t dst, int x) {  // x-th transfer
-    if (x < kLatPerWave) {
-      const int n = 4 * x + wave_u;
-      dma16_if(go, dst + uint32_t(n * kLatB), lat_off(x), g + size_t(n) * kRowB);
-    } else {
-      dma16_if(go, dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), g + size_t(8 * wave_u) * kRowB);
-    }
-  };
-  auto dma_tile = [&](int k) {
-    const unsigned char* g = tile_src(k);
-    const uint32_t dst = lds0 + uint32_t((k % kNBuf) * kTileB);
-#pragma unroll
-    for (int x = 0; x < kDmaPerWave; ++x) dma_one(1u, g, dst, x);
-  };
-
-  dma_tile(0);
-
-  // ---- this wave's 32 heads of q_hat, as the B operand of S^T = tile . q_hat^T: the 512 latent
-  // columns stay in registers; the 64 rotary columns of all heads go to LDS (swizzled like the
-  // tile's rotary rows), which keeps the register file within budget.
-  bf16x8 qf[kKLat];
-  {
-    const uint16_t* qrow = q_hat + (size_t(b) * kH + head) * kW + 8 * hi;
-#pragma unroll
-    for (int k = 0; k < kKLat; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k);
-    const uint16_t* qb = q_hat + size_t(b) * kH * kW + kDc;
-#pragma unroll
-    for (int x = 0; x < kH * kRopeB / 16 / kThreads; ++x) {  // 4 chunks of 16 B per thread
-      const int c = threadIdx.x + x * kThreads, h = c >> 3, ch = c & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qb + size_t(h) * kW + 8 * ch);
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + kQrOff + h * kRopeB + 16 * (ch ^ rope_swz(h))) = v;
-    }
-  }
-  // Consume these loads here: an empty asm that reads every fragment makes the compiler wait for
-  // them before the tile loop (tile 0 lands too).  Otherwise its waits for them land inside the
-  // loop, where the vmcnt they use would also drain the tile transfers in flight.
-#pragma unroll
-  for (int k = 0; k < kKLat; ++k) asm volatile("" : "+v"(qf[k]));
-  if (ntiles > 1) dma_tile(1);
 
   // ---- per-lane LDS offsets
   // score reads: row (lane&31), logical chunk 2k + hi (latent) or 2(k-32) + hi (rotary).  The
@@ -233,147 +188,261 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  f32x16 acc[kMBlk];
-  float m_ref = -INFINITY, m_max = -INFINITY, l_lane = 0.f;
-  bf16x8 pb0, pb1;  // probabilities of the previous tile, bf16, k-steps 0 and 1
+  // ---- the segment list
+  const int unit = blockIdx.x;
+  int next_b, next_cb = 0, unit_end = 0, quota = 0;
+  if constexpr (kBalanced) {
+    int total;
+    sched_prefix(seq_lens, batch, cap, 0, next_cb, total);
+    total = __builtin_amdgcn_readfirstlane(total);  // wave-uniform: keep the segment loop scalar
+    quota = sched_quota(total, n_splits);
+    if (quota == 0 || unit * quota >= total) return;  // idle unit (uniform)
+    unit_end = min(unit * quota + quota, total);
+    sched_find(seq_lens, batch, cap, unit * quota, next_b, next_cb);
+    next_b = __builtin_amdgcn_readfirstlane(next_b);
+    next_cb = __builtin_amdgcn_readfirstlane(next_cb);
+  } else {
+    next_b = blockIdx.y;
+  }
 
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass > 0) {
-      dma_tile(0);
-      if (ntiles > 1) dma_tile(1);
+  for (bool first_seg = true;; first_seg = false) {
+    int b, t0, t1;
+    size_t slot;
+    if constexpr (kBalanced) {
+      if (next_b >= batch || next_cb >= unit_end) break;
+      b = next_b;
+      const int len = sched_len(seq_lens[b], cap);
+      int k0, k1;
+      sched_segment(next_cb, sched_tiles(len), unit, quota, k0, k1);
+      next_cb += sched_cost(len);
+      ++next_b;
+      if (k1 <= k0) continue;  // this unit holds only the segment price of sequence b
+      t0 = k0 * kTile;
+      t1 = min(k1 * kTile, len);
+      slot = size_t(unit) + b;
+    } else {
+      b = next_b;
+      t0 = unit * split_tokens;
+      t1 = min(t0 + split_tokens, sched_len(seq_lens[b], cap));
+      slot = size_t(b) * n_splits + unit;
+      if (t0 >= t1) {  // empty chunk: lse = -inf; its o_part is never read by the combine
+        if (hi == 0) lse_part[slot * kH + head] = -INFINITY;
+        return;
+      }
     }
+    if (!first_seg) __syncthreads();  // the previous segment is done with every LDS buffer
+    const size_t orow = slot * kH + head;
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+
+    // Page ids of the segment, 64 per window, one per lane.  t0 is a multiple of the tile.
+    const int kt0 = t0 / kTile;  // first tile, counted from the sequence start
+    const int p0 = kt0 >> tiles_per_page_log2;
+    const int npg = ((kt0 + ntiles - 1) >> tiles_per_page_log2) - p0 + 1;
+    const int32_t* pt_row = page_table + size_t(b) * max_pages;
+    int wbase = 0;  // first page of the window held in my_page
+    int my_page = load_page_window(pt_row, p0, npg, max_pages, lane);
+    auto tile_src = [&](int k) {
+      const int kt = kt0 + k;
+      const int pg = __builtin_amdgcn_readlane(my_page, ((kt >> tiles_per_page_log2) - p0 - wbase) & 63);
+      const int in_page = (kt & ((1 << tiles_per_page_log2) - 1)) * kTile;
+      return reinterpret_cast<const unsigned char*>(pool + (size_t(pg) * page_size + in_page) * kW);
+    };
+    auto dma_one = [&](uint32_t go, const unsigned char* g, uint32_t dst, int x) {  // x-th transfer
+      if (x < kLatPerWave) {
+        const int n = 4 * x + wave_u;
+        dma16_if(go, dst + uint32_t(n * kLatB), lat_off(x), g + size_t(n) * kRowB);
+      } else {
+        dma16_if(go, dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), g + size_t(8 * wave_u) * kRowB);
+      }
+    };
+    auto dma_tile = [&](int k) {
+      const unsigned char* g = tile_src(k);
+      const uint32_t dst = lds0 + uint32_t((k % kNBuf) * kTileB);
 #pragma unroll
-    for (int mb = 0; mb < kMBlk; ++mb)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[mb][x] = 0.f;
-    l_lane = 0.f;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      pb0[x] = (__bf16)0.f;
-      pb1[x] = (__bf16)0.f;
-    }
-    // The weighted sum of the tile before tile 0 runs on a zeroed buffer with zero probabilities,
-    // which keeps the pipelined loop uniform.
+      for (int x = 0; x < kDmaPerWave; ++x) dma_one(1u, g, dst, x);
+    };
+
+    dma_tile(0);
+
+    // ---- this wave's 32 heads of q_hat, as the B operand of S^T = tile . q_hat^T: the 512 latent
+    // columns stay in registers; the 64 rotary columns of all heads go to LDS (swizzled like the
+    // tile's rotary rows), which keeps the register file within budget.
+    bf16x8 qf[kKLat];
     {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      for (int x = threadIdx.x; x < kRopeOff / 16; x += kThreads)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + (kNBuf - 1) * kTileB + 16 * x) = zero;
+      const uint16_t* qrow = q_hat + (size_t(b) * kH + head) * kW + 8 * hi;
+#pragma unroll
+      for (int k = 0; k < kKLat; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k);
+      const uint16_t* qb = q_hat + size_t(b) * kH * kW + kDc;
+#pragma unroll
+      for (int x = 0; x < kH * kRopeB / 16 / kThreads; ++x) {  // 4 chunks of 16 B per thread
+        const int c = threadIdx.x + x * kThreads, h = c >> 3, ch = c & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + size_t(h) * kW + 8 * ch);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + kQrOff + h * kRopeB + 16 * (ch ^ rope_swz(h))) = v;
+      }
     }
+    // Consume these loads here: an empty asm that reads every fragment makes the compiler wait for
+    // them before the tile loop (tile 0 and the previous segment's stores complete too).  Otherwise
+    // its waits for them land inside the loop, where the vmcnt they use would also drain the tile
+    // transfers in flight.
+#pragma unroll
+    for (int k = 0; k < kKLat; ++k) asm volatile("" : "+v"(qf[k]));
+    if (ntiles > 1) dma_tile(1);
 
-    bool over = false;
-    for (int j = 0; j < ntiles; ++j) {
-      if (j + 1 < ntiles)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");  // tile j landed, j+1 may fly
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // every wave's part of tile j landed; tile j-2 fully consumed
-      // Keep the per-step offsets derived inside the loop (one XOR each) instead of letting the
-      // compiler hoist a dozen precomputed copies into registers next to the q_hat fragments.
-      asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(qq_x), "+v"(pv_x), "+v"(pv_d8));
-      lds_u8* const tb = lbase + (j % kNBuf) * kTileB;
-      lds_u8* const tp = lbase + ((j + kNBuf - 1) % kNBuf) * kTileB;
-      const int nvalid = min(kTile, t1 - (t0 + j * kTile));
-      if (nvalid < kTile) {  // tail tile: latent rows past the sequence end read as zeros
+    f32x16 acc[kMBlk];
+    float m_ref = -INFINITY, m_max = -INFINITY, l_lane = 0.f;
+    bf16x8 pb0, pb1;  // probabilities of the previous tile, bf16, k-steps 0 and 1
+
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass > 0) {
+        if (wbase != 0) {
+          wbase = 0;
+          my_page = load_page_window(pt_row, p0, npg, max_pages, lane);
+        }
+        dma_tile(0);
+        if (ntiles > 1) dma_tile(1);
+      }
+#pragma unroll
+      for (int mb = 0; mb < kMBlk; ++mb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[mb][x] = 0.f;
+      l_lane = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        pb0[x] = (__bf16)0.f;
+        pb1[x] = (__bf16)0.f;
+      }
+      // The weighted sum of the tile before tile 0 runs on a zeroed buffer with zero
+      // probabilities, which keeps the pipelined loop uniform.
+      {
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        for (int x = threadIdx.x; x < (kTile - nvalid) * (kLatB / 16); x += kThreads)
-          *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tb + nvalid * kLatB + 16 * x) = zero;
-        __syncthreads();
-      }
-      const uint32_t dma_next = __builtin_amdgcn_readfirstlane(j + 2 < ntiles ? 1u : 0u);
-      const unsigned char* gnext = tile_src(dma_next ? j + 2 : j);  // never look past the chunk
-      const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
-
-      // ---- scores of tile j interleaved with the weighted sum of tile j-1
-      f32x16 sacc;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
-      bf16x8 qa[3], pa[3], qb[3];  // operands loaded two steps ahead (qb: rotary q_hat steps)
-      auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
-      qa[0] = lds16(a_src(tb, 0));
-      pa[0] = tr8(tp, 0);
-      qa[1] = lds16(a_src(tb, 1));
-      pa[1] = tr8(tp, 1);
-#pragma unroll
-      for (int i = 0; i < kKSteps; ++i) {
-        if (i + 2 < kKSteps) {
-          qa[(i + 2) % 3] = lds16(a_src(tb, i + 2));
-          if (i + 2 >= kKLat) qb[(i + 2) % 3] = lds16(b_src(i + 2));
-        }
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % 3], i < kKLat ? qf[i] : qb[i % 3], sacc, 0, 0, 0);
-        if (i < kPvSteps) {
-          if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
-          acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15],
-                                                                0, 0, 0);
-        }
-        if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);  // nine transfers of tile j+2
-        __builtin_amdgcn_sched_barrier(0);
+        for (int x = threadIdx.x; x < kRopeOff / 16; x += kThreads)
+          *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + (kNBuf - 1) * kTileB + 16 * x) = zero;
       }
 
-      // ---- online softmax of tile j (base-2 logits); lane = one head, lanes (l, l^32) share it
-      if (nvalid < kTile) {
+      bool over = false;
+      for (int j = 0; j < ntiles; ++j) {
+        if (j + 1 < ntiles)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");  // tile j landed, j+1 may fly
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave's part of tile j landed; tile j-2 fully consumed
+        // Keep the per-step offsets derived inside the loop (one XOR each) instead of letting the
+        // compiler hoist a dozen precomputed copies into registers next to the q_hat fragments.
+        asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(qq_x), "+v"(pv_x), "+v"(pv_d8));
+        lds_u8* const tb = lbase + (j % kNBuf) * kTileB;
+        lds_u8* const tp = lbase + ((j + kNBuf - 1) % kNBuf) * kTileB;
+        const int nvalid = min(kTile, t1 - (t0 + j * kTile));
+        if (nvalid < kTile) {  // tail tile: latent rows past the sequence end read as zeros
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          for (int x = threadIdx.x; x < (kTile - nvalid) * (kLatB / 16); x += kThreads)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tb + nvalid * kLatB + 16 * x) = zero;
+          __syncthreads();
+        }
+        // tiles left after tile j+1: nonzero when tile j+2 is to be fetched.  A count, not a
+        // flag: a boolean would be narrowed to a lane mask and leave the scalar operand it feeds.
+        const uint32_t dma_next = __builtin_amdgcn_readfirstlane(uint32_t(max(ntiles - j - 2, 0)));
+        // A segment longer than 64 pages moves its page window once tile j+2 leaves it (the wait
+        // inside the load also drains tile j+1, a bubble every 64 pages).
+        if (dma_next && ((kt0 + j + 2) >> tiles_per_page_log2) - p0 - wbase >= 64) {
+          wbase += 64;
+          my_page = load_page_window(pt_row, p0 + wbase, npg - wbase, max_pages, lane);
+        }
+        const unsigned char* gnext = tile_src(dma_next ? j + 2 : j);  // never look past the segment
+        const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
+
+        // ---- scores of tile j interleaved with the weighted sum of tile j-1
+        f32x16 sacc;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
+        bf16x8 qa[3], pa[3], qb[3];  // operands loaded two steps ahead (qb: rotary q_hat steps)
+        auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
+        qa[0] = lds16(a_src(tb, 0));
+        pa[0] = tr8(tp, 0);
+        qa[1] = lds16(a_src(tb, 1));
+        pa[1] = tr8(tp, 1);
+#pragma unroll
+        for (int i = 0; i < kKSteps; ++i) {
+          if (i + 2 < kKSteps) {
+            qa[(i + 2) % 3] = lds16(a_src(tb, i + 2));
+            if (i + 2 >= kKLat) qb[(i + 2) % 3] = lds16(b_src(i + 2));
+          }
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % 3], i < kKLat ? qf[i] : qb[i % 3], sacc, 0, 0, 0);
+          if (i < kPvSteps) {
+            if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
+            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15],
+                                                                  0, 0, 0);
+          }
+          if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);  // nine transfers of tile j+2
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- online softmax of tile j (base-2 logits); lane = one head, lanes (l, l^32) share it
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
+            if (tok >= nvalid) sacc[x] = -INFINITY;
+          }
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
+        mx = lane_swap_max(mx);
+        if (pass == 0 && j == 0) m_ref = mx;  // the segment's first tile fixes the reference
+        m_max = fmaxf(m_max, mx);
+        over |= mx > m_ref + kRerunMargin;
+        float pr[16];
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
-          if (tok >= nvalid) sacc[x] = -INFINITY;
+          pr[x] = fast_exp2(sacc[x] - m_ref);
+          l_lane += pr[x];
+        }
+        pb0 = pack8(&pr[0]);
+        pb1 = pack8(&pr[8]);
+      }
+
+      // ---- weighted sum of the last tile
+      {
+        lds_u8* const tp = lbase + ((ntiles - 1) % kNBuf) * kTileB;
+        bf16x8 pa[3];
+        pa[0] = tr8(tp, 0);
+        pa[1] = tr8(tp, 1);
+#pragma unroll
+        for (int i = 0; i < kPvSteps; ++i) {
+          if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
+          acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      float mx = sacc[0];
-#pragma unroll
-      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
-      mx = lane_swap_max(mx);
-      if (pass == 0 && j == 0) m_ref = mx;  // the chunk's first tile fixes the reference
-      m_max = fmaxf(m_max, mx);
-      over |= mx > m_ref + kRerunMargin;
-      float pr[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        pr[x] = fast_exp2(sacc[x] - m_ref);
-        l_lane += pr[x];
-      }
-      pb0 = pack8(&pr[0]);
-      pb1 = pack8(&pr[8]);
+
+      // ---- rerun the segment if some head outgrew its reference (uniform decision)
+      // the flags go to the buffer after the last tile's, idle now
+      __attribute__((address_space(3))) int* rerun_flag =
+          reinterpret_cast<__attribute__((address_space(3))) int*>(lbase + (ntiles % kNBuf) * kTileB);
+      const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+      if (lane == 0) rerun_flag[wave] = wave_over;
+      __syncthreads();
+      const bool rerun = rerun_flag[0] | rerun_flag[1] | rerun_flag[2] | rerun_flag[3];
+      if (!rerun) break;
+      m_ref = m_max;
+      __syncthreads();
     }
 
-    // ---- weighted sum of the last tile
-    {
-      lds_u8* const tp = lbase + ((ntiles - 1) % kNBuf) * kTileB;
-      bf16x8 pa[3];
-      pa[0] = tr8(tp, 0);
-      pa[1] = tr8(tp, 1);
+    // ---- normalise and write the segment's partial
+    const float l_tot = lane_swap_sum(l_lane);
+    const float inv = 1.f / l_tot;
+    float* op = o_part + orow * kDc + 4 * hi;
 #pragma unroll
-      for (int i = 0; i < kPvSteps; ++i) {
-        if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
-        acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int mb = 0; mb < kMBlk; ++mb) {
+      const f32x16 v = acc[mb] * inv;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        *reinterpret_cast<float4*>(op + 32 * mb + 8 * j4) = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // ---- rerun the chunk if some head outgrew its reference (uniform decision)
-    // the flags go to the buffer after the last tile's, idle now
-    __attribute__((address_space(3))) int* rerun_flag =
-        reinterpret_cast<__attribute__((address_space(3))) int*>(lbase + (ntiles % kNBuf) * kTileB);
-    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-    if (lane == 0) rerun_flag[wave] = wave_over;
-    __syncthreads();
-    const bool rerun = rerun_flag[0] | rerun_flag[1] | rerun_flag[2] | rerun_flag[3];
-    if (!rerun) break;
-    m_ref = m_max;
-    __syncthreads();
+    if (hi == 0) lse_part[orow] = (m_ref + log2f(l_tot)) * kLn2;
+    if constexpr (!kBalanced) break;
   }
-
-  // ---- normalise and write the chunk's partial
-  const float l_tot = lane_swap_sum(l_lane);
-  const float inv = 1.f / l_tot;
-  float* op = o_part + orow * kDc + 4 * hi;
-#pragma unroll
-  for (int mb = 0; mb < kMBlk; ++mb) {
-    const f32x16 v = acc[mb] * inv;
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4)
-      *reinterpret_cast<float4*>(op + 32 * mb + 8 * j4) = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (hi == 0) lse_part[orow] = (m_ref + log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -381,17 +450,26 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
 bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens) {
   const int tpp = c.page_size / kTile;  // tiles per page: a power of two
   return d.dtype == MLA_BF16 && d.H == kH && d.dc == kDc && d.dr == kW - kDc && c.page_size % kTile == 0 &&
-         tpp > 0 && (tpp & (tpp - 1)) == 0 && split_tokens % c.page_size == 0 &&
-         split_tokens <= 64 * c.page_size;
+         tpp > 0 && (tpp & (tpp - 1)) == 0 && (split_tokens == 0 || split_tokens % c.page_size == 0);
 }
 
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
                               float* o_part, float* lse_part, hipStream_t s) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
-      static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.max_pages, c.page_size, tpp_log2,
+  decode_mfma_kernel<false><<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), n_splits, split_tokens, o_part, lse_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
+                                       float* lse_part, hipStream_t s) {
+  (void)d;
+  const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
+  decode_mfma_kernel<true><<<dim3(n_units), kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
+      static_cast<const uint16_t*>(q_hat), n_units, 0, o_part, lse_part);
   return hipGetLastError();
 }
 

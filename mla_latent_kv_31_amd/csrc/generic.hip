@@ -10,6 +10,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mla {
 
@@ -48,10 +49,13 @@ __global__ __launch_bounds__(kThreads) void absorb_generic_kernel(Dims d, const 
 }
 
 // -------------------------------------------------------------------------------- attend
-// One block per (chunk or query row, sequence, head).  Online softmax over the key range in
+// One block per (chunk or query row or unit, sequence, head).  Online softmax over the key range in
 // tiles of 256 tokens: every thread scores one token, then every thread accumulates its latent
-// columns over the tile.  PREFILL: blockIdx.x is the query row, keys t <= q_start + row.
-template <typename T, bool PREFILL>
+// columns over the tile.  MODE kPrefill: blockIdx.x is the query row, keys t <= q_start + row.
+// MODE kBalanced: blockIdx.x is a unit of the balanced split (schedule.h); a block whose segment
+// is empty writes nothing.
+enum { kFixed = 0, kPrefill = 1, kBalanced = 2 };
+template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache c, const T* __restrict__ q_hat,
                                                                   int split_tokens, int n_splits, int q_len,
                                                                   const int32_t* __restrict__ q_start,
@@ -63,14 +67,24 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache 
   float* ps = sm + W;           // [kThreads]
   float* red = ps + kThreads;   // [16]
   const int x = blockIdx.x, b = blockIdx.y, h = blockIdx.z;
-  const int len = c.seq_lens[b];
+  const int len = sched_len(c.seq_lens[b], c.max_pages * c.page_size);
   int t0, t1;
   size_t qrow, orow;
-  if (PREFILL) {
+  if (MODE == kPrefill) {
     t0 = 0;
     t1 = min(len, q_start[b] + x + 1);
     qrow = (size_t(b) * q_len + x) * d.H + h;
     orow = qrow;
+  } else if (MODE == kBalanced) {
+    int cb, total;
+    sched_prefix(c.seq_lens, c.batch, c.max_pages * c.page_size, b, cb, total);
+    int k0, k1;
+    sched_segment(cb, sched_tiles(len), x, sched_quota(total, n_splits), k0, k1);
+    if (k1 <= k0) return;  // uniform over the block
+    t0 = k0 * kSchedTile;
+    t1 = min(k1 * kSchedTile, len);
+    qrow = size_t(b) * d.H + h;
+    orow = (size_t(x) + b) * d.H + h;
   } else {
     t0 = x * split_tokens;
     t1 = min(t0 + split_tokens, len);
@@ -124,17 +138,34 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache 
 }
 
 // -------------------------------------------------------------------------------- combine
-// One block per (head, sequence): LSE-weighted merge of the split partials.
-__global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, int S, const float* __restrict__ o_part,
+// One block per (head, sequence): LSE-weighted merge of the sequence's partials, the S chunks of
+// the fixed split or the segment slots of the balanced split (schedule.h).
+template <bool BAL>
+__global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache c, int S, const float* __restrict__ o_part,
                                                                    const float* __restrict__ lse_part,
                                                                    float* __restrict__ z,
                                                                    float* __restrict__ lse_out) {
   __shared__ float red[16];
   __shared__ float wts[1024];
   const int h = blockIdx.x, b = blockIdx.y;
-  const float* lp = lse_part + size_t(b) * S * d.H + h;  // stride H over splits
+  size_t base = size_t(b) * S;
+  int count = S;
+  if (BAL) {
+    const int cap = c.max_pages * c.page_size;
+    int cb, total;
+    sched_prefix(c.seq_lens, c.batch, cap, b, cb, total);
+    const int tiles = sched_tiles(sched_len(c.seq_lens[b], cap));
+    count = 0;
+    if (tiles > 0) {
+      int w0, w1;
+      sched_units(cb, tiles, sched_quota(total, S), w0, w1);
+      base = size_t(w0) + b;
+      count = w1 - w0 + 1;
+    }
+  }
+  const float* lp = lse_part + base * d.H + h;  // stride H over partials
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) mx = fmaxf(mx, lp[size_t(s) * d.H]);
+  for (int s = threadIdx.x; s < count; s += blockDim.x) mx = fmaxf(mx, lp[size_t(s) * d.H]);
   mx = block_max(mx, red);
   float* zo = z + (size_t(b) * d.H + h) * d.dc;
   if (mx == -INFINITY) {
@@ -143,21 +174,21 @@ __global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, int S
     return;
   }
   float tot = 0.f;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) tot += expf(lp[size_t(s) * d.H] - mx);
+  for (int s = threadIdx.x; s < count; s += blockDim.x) tot += expf(lp[size_t(s) * d.H] - mx);
   tot = block_sum(tot, red);
   const float inv = 1.f / tot;
   float acc[kGenericMaxDc / kThreads];
 #pragma unroll
   for (int i = 0; i < kGenericMaxDc / kThreads; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 1024) {
-    const int ns = min(1024, S - s0);
+  for (int s0 = 0; s0 < count; s0 += 1024) {
+    const int ns = min(1024, count - s0);
     __syncthreads();
     for (int s = threadIdx.x; s < ns; s += blockDim.x) wts[s] = expf(lp[size_t(s0 + s) * d.H] - mx) * inv;
     __syncthreads();
     for (int s = 0; s < ns; ++s) {
       const float w = wts[s];
       if (w == 0.f) continue;  // empty chunk: its partial is never read
-      const float* op = o_part + ((size_t(b) * S + s0 + s) * d.H + h) * d.dc;
+      const float* op = o_part + ((base + s0 + s) * d.H + h) * d.dc;
 #pragma unroll
       for (int i = 0; i < kGenericMaxDc / kThreads; ++i) {
         const int j = threadIdx.x + i * kThreads;
@@ -285,10 +316,10 @@ hipError_t launch_decode_generic(const Dims& d, const Cache& c, const void* q_ha
   const dim3 grid(n_splits, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, false><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, split_tokens,
+    attend_generic_kernel<uint16_t, kFixed><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, split_tokens,
                                                                        n_splits, 1, nullptr, o_part, lse_part);
   else
-    attend_generic_kernel<float, false><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, split_tokens, n_splits,
+    attend_generic_kernel<float, kFixed><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, split_tokens, n_splits,
                                                                     1, nullptr, o_part, lse_part);
   return hipGetLastError();
 }
@@ -298,17 +329,37 @@ hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_h
   const dim3 grid(q_len, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, true><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, 0, 1, q_len,
+    attend_generic_kernel<uint16_t, kPrefill><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, 0, 1, q_len,
                                                                       q_start, z, lse);
   else
-    attend_generic_kernel<float, true><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, 1, q_len, q_start,
+    attend_generic_kernel<float, kPrefill><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, 1, q_len, q_start,
                                                                    z, lse);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_generic(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                   float* z, float* lse, hipStream_t s) {
-  combine_generic_kernel<<<dim3(d.H, batch), kThreads, 0, s>>>(d, n_splits, o_part, lse_part, z, lse);
+  Cache none{};
+  combine_generic_kernel<false><<<dim3(d.H, batch), kThreads, 0, s>>>(d, none, n_splits, o_part, lse_part, z, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units,
+                                          float* o_part, float* lse_part, hipStream_t s) {
+  const dim3 grid(n_units, c.batch, d.H);
+  const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
+  if (d.dtype == MLA_BF16)
+    attend_generic_kernel<uint16_t, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, 0, n_units, 1,
+                                                                          nullptr, o_part, lse_part);
+  else
+    attend_generic_kernel<float, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, n_units, 1,
+                                                                       nullptr, o_part, lse_part);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+                                           const float* lse_part, float* z, float* lse, hipStream_t s) {
+  combine_generic_kernel<true><<<dim3(d.H, c.batch), kThreads, 0, s>>>(d, c, n_units, o_part, lse_part, z, lse);
   return hipGetLastError();
 }
 

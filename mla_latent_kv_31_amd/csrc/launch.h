@@ -28,10 +28,13 @@ constexpr int kGenericMaxDc = 1024;   // latent width handled by the generic dec
 constexpr int kGenericMaxRow = 2048;  // d_c + d_r
 constexpr int kGenericMaxDk = 1024;
 
-// ---- bf16 MFMA decode for the DeepSeek-V3 shape (128 heads, d_c 512, d_r 64, 64-token tiles)
+// ---- bf16 MFMA decode for the DeepSeek-V3 shape (128 heads, d_c 512, d_r 64, 32-token tiles).
+// split_tokens == 0 asks about the balanced split.
 bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens);
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
                               float* o_part, float* lse_part, hipStream_t s);
+hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
+                                       float* lse_part, hipStream_t s);
 
 // ---- bf16 MFMA per-head projections (d_c 512, d_k = d_v = 128) and the vectorised combine
 bool proj_mfma_supported(const Dims& d);
@@ -42,6 +45,8 @@ hipError_t launch_out_proj_mfma(const Dims& d, const float* z, const void* w_uv,
 bool combine_fast_supported(const Dims& d, int n_splits);
 hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                float* z, float* lse, hipStream_t s);
+hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+                                        const float* lse_part, float* z, float* lse, hipStream_t s);
 
 hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
                                  const int32_t* pos, int rows, void* q_hat, hipStream_t s);
@@ -51,6 +56,10 @@ hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_h
                                   const int32_t* q_start, float* z, float* lse, hipStream_t s);
 hipError_t launch_combine_generic(const Dims& d, int batch, int n_splits, const float* o_part,
                                   const float* lse_part, float* z, float* lse, hipStream_t s);
+hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units,
+                                          float* o_part, float* lse_part, hipStream_t s);
+hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+                                           const float* lse_part, float* z, float* lse, hipStream_t s);
 hipError_t launch_out_proj_generic(const Dims& d, const float* z, const void* w_uv, int rows, float* out,
                                    hipStream_t s);
 hipError_t launch_project_query(const Dims& d, int d_model, int d_cq, const void* h, const void* w_dq,

@@ -1,0 +1,95 @@
+// Work-balanced split of a decode batch, shared by the decode and combine kernels.
+//
+// Every sequence costs tiles + MLA_BALANCED_SEG_COST (0 when empty), with tiles = ceil(len / 32);
+// the costs are laid end to end in batch order, and unit w of n owns the cost range
+// [w*q, (w+1)*q) with q = ceil(total / n).  The first MLA_BALANCED_SEG_COST cost positions of a
+// sequence stand for the fixed price of one segment (query load, pipeline fill, partial write);
+// its tiles follow.  The segment of sequence b in unit w is the set of b's tiles inside w's
+// range; its partial goes to slot w + b, which no other non-empty segment shares.  Both sides
+// derive everything from seq_lens, so no schedule is stored anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+constexpr int kSchedTile = MLA_BALANCED_TILE;
+constexpr int kSchedSegCost = MLA_BALANCED_SEG_COST;
+
+__host__ __device__ inline int sched_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
+__host__ __device__ inline int sched_tiles(int len) { return (len + kSchedTile - 1) / kSchedTile; }
+__host__ __device__ inline int sched_cost(int len) {
+  const int t = sched_tiles(len);
+  return t > 0 ? t + kSchedSegCost : 0;
+}
+__host__ __device__ inline int sched_quota(int total, int n_units) { return (total + n_units - 1) / n_units; }
+
+// Tiles [k0, k1) of a sequence (cost prefix cb, `tiles` tiles) inside unit w; empty when k1 <= k0.
+__host__ __device__ inline void sched_segment(int cb, int tiles, int w, int q, int& k0, int& k1) {
+  const int s = cb + kSchedSegCost;
+  const int lo = w * q, hi = lo + q;
+  k0 = (lo > s ? lo : s) - s;
+  k1 = (hi < s + tiles ? hi : s + tiles) - s;
+}
+
+// Units whose segments of a non-empty sequence are non-empty: [w0, w1].
+__host__ __device__ inline void sched_units(int cb, int tiles, int q, int& w0, int& w1) {
+  const int s = cb + kSchedSegCost;
+  w0 = s / q;
+  w1 = (s + tiles - 1) / q;
+}
+
+// ---- wave-cooperative helpers (wave64); every lane receives the results
+
+__device__ inline int sched_wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Cost prefix of sequence b and the total cost of the batch.
+__device__ inline void sched_prefix(const int32_t* __restrict__ seq_lens, int batch, int cap, int b, int& cb,
+                                    int& total) {
+  const int lane = threadIdx.x & 63;
+  int before = 0, all = 0;
+  for (int i = lane; i < batch; i += 64) {
+    const int c = sched_cost(sched_len(seq_lens[i], cap));
+    all += c;
+    if (i < b) before += c;
+  }
+  cb = sched_wave_sum(before);
+  total = sched_wave_sum(all);
+}
+
+// First sequence whose cost range ends past `pos`, with its cost prefix (batch and the total
+// cost when there is none).
+__device__ inline void sched_find(const int32_t* __restrict__ seq_lens, int batch, int cap, int pos, int& b,
+                                  int& cb) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c0 = 0; c0 < batch; c0 += 64) {
+    const int i = c0 + lane;
+    const int c = i < batch ? sched_cost(sched_len(seq_lens[i], cap)) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const uint64_t m = __ballot(i < batch && base + incl > pos);
+    if (m) {
+      const int f = __builtin_ctzll(m);
+      b = c0 + f;
+      cb = base + __shfl(incl - c, f, 64);
+      return;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  b = batch;
+  cb = base;
+}
+
+}  // namespace mla

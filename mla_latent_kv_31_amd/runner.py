@@ -5,6 +5,8 @@ entry points in order; all arithmetic runs in libmla.so.
 
 Decode step (one query token per sequence):
     mla_absorb_query -> mla_decode_partial -> mla_combine -> mla_out_proj
+or, with the work-balanced split over ``n_units`` workgroups:
+    mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced -> mla_out_proj
 Chunked prefill (q_len query tokens per sequence):
     mla_absorb_query -> mla_prefill_chunk -> mla_out_proj
 """
@@ -29,15 +31,33 @@ def _torch_dtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
+def compute_units(device=None) -> int:
+    """Compute units of the device (one balanced-split unit each)."""
+    return int(torch.cuda.get_device_properties(torch.device(device or "cuda:0")).multi_processor_count)
+
+
+def balanced_units(lens, n_cu: int, min_tiles: int = 16) -> int:
+    """Units of the balanced split for a batch: one per compute unit, fewer when that would leave
+    a unit less than `min_tiles` tiles (MLA_BALANCED_TILE tokens each) of cache to read."""
+    lens = np.asarray(lens, dtype=np.int64)
+    tiles = int(np.sum((lens + L.MLA_BALANCED_TILE - 1) // L.MLA_BALANCED_TILE))
+    return max(1, min(int(n_cu), L.MLA_BALANCED_MAX_UNITS, -(-tiles // min_tiles)))
+
+
 def dims_for(w, flags: int = 0) -> L.MlaDims:
     return L.dims(w.n_heads, w.d_c, w.d_r, w.d_k, w.d_v, dtype=L.MLA_BF16 if w.dtype == "bf16" else L.MLA_F32,
                   rope_base=w.rope_base, sm_scale=0.0, flags=flags)
 
 
 class DecodeStep:
-    """All device buffers of one batched decode step; ``run()`` enqueues the four calls."""
+    """All device buffers of one batched decode step; ``run()`` enqueues the four calls.
 
-    def __init__(self, inp: dict, split_tokens: int, device="cuda:0", flags: int = 0, max_len: int | None = None):
+    ``split_tokens`` > 0 selects fixed chunks of that many tokens; ``n_units`` selects the
+    work-balanced split instead (``split_tokens`` is then ignored).
+    """
+
+    def __init__(self, inp: dict, split_tokens: int = 0, device="cuda:0", flags: int = 0,
+                 max_len: int | None = None, n_units: int | None = None):
         w = inp["workload"]
         self.w = w
         self.device = torch.device(device)
@@ -53,13 +73,20 @@ class DecodeStep:
         self.pos = to_device(inp["pos"].astype(np.int32), dev)
         self.B = int(inp["lens"].shape[0])
         self.max_len = int(inp["lens"].max()) if max_len is None else int(max_len)
-        self.split_tokens = int(split_tokens)
-        self.S = L.mla_decode_num_splits(self.max_len, self.split_tokens)
         H, W = w.n_heads, w.d_c + w.d_r
+        self.n_units = None if n_units is None else int(n_units)
+        if self.n_units is not None:
+            self.split_tokens = 0
+            self.S = L.mla_balanced_num_slots(self.B, self.n_units)
+            part_shape = (max(self.S, 1),)
+        else:
+            self.split_tokens = int(split_tokens)
+            self.S = L.mla_decode_num_splits(self.max_len, self.split_tokens)
+            part_shape = (self.B, self.S)
         td = _torch_dtype(w.dtype)
         self.q_hat = torch.empty((self.B, H, W), dtype=td, device=dev)
-        self.o_part = torch.empty((self.B, self.S, H, w.d_c), dtype=torch.float32, device=dev)
-        self.lse_part = torch.empty((self.B, self.S, H), dtype=torch.float32, device=dev)
+        self.o_part = torch.empty(part_shape + (H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty(part_shape + (H,), dtype=torch.float32, device=dev)
         self.z = torch.empty((self.B, H, w.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.B, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, H, w.d_v), dtype=torch.float32, device=dev)
@@ -72,11 +99,19 @@ class DecodeStep:
         L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.pos, self.B, self.q_hat, stream)
 
     def attend(self, stream=None):
-        L.mla_decode_partial(self.d, self.c, self.q_hat, self.max_len, self.split_tokens, self.o_part,
-                             self.lse_part, stream)
+        if self.n_units is not None:
+            L.mla_decode_partial_balanced(self.d, self.c, self.q_hat, self.n_units, self.o_part, self.lse_part,
+                                          stream)
+        else:
+            L.mla_decode_partial(self.d, self.c, self.q_hat, self.max_len, self.split_tokens, self.o_part,
+                                 self.lse_part, stream)
 
     def combine(self, stream=None):
-        L.mla_combine(self.d, self.B, self.S, self.o_part, self.lse_part, self.z, self.lse, stream)
+        if self.n_units is not None:
+            L.mla_combine_balanced(self.d, self.c, self.n_units, self.o_part, self.lse_part, self.z, self.lse,
+                                   stream)
+        else:
+            L.mla_combine(self.d, self.B, self.S, self.o_part, self.lse_part, self.z, self.lse, stream)
 
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B, self.out, stream)

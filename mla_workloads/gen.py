@@ -96,8 +96,8 @@ WORKLOADS: dict[str, Workload] = {
         random_pages=True, split_tokens=2048,
         notes="batch 64, lengths uniform on [1024, 32768], 64-token pages, random page table"),
     "v3_b4_ctx128k": Workload(
-        name="v3_b4_ctx128k", seed=4, kind="decode", batch=4, ctx=131072, split_tokens=512,
-        notes="batch 4, 131,072 tokens each, split-K into 256 chunks per sequence"),
+        name="v3_b4_ctx128k", seed=4, kind="decode", batch=4, ctx=131072, split_tokens=2048,
+        notes="batch 4, 131,072 tokens each, split-K into 256 chunks over the batch (64 per sequence)"),
     "v3_prefill_b2": Workload(
         name="v3_prefill_b2", seed=5, kind="prefill", batch=2, ctx=2048, q_len=512,
         notes="2,048 prior tokens + a 512-token causal chunk already appended to the cache"),

@@ -134,3 +134,31 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(16)
     with pytest.raises(ValueError):
         M.mla_out_proj(d, x, x, 1, x, stream=0)
+
+
+def test_balanced_validation():
+    lib = M.library()
+    d = _dims()
+    assert M.mla_balanced_num_slots(64, 256) == 319
+    assert M.mla_balanced_num_slots(0, 256) == 0
+    assert M.mla_balanced_num_slots(4, 0) == -1
+    assert M.mla_balanced_num_slots(4, M.MLA_BALANCED_MAX_UNITS + 1) == -1
+
+    def dec(c, n=256, q=A, o=B_, lse=B_):
+        return lib.mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), q, n, o, lse, None)
+
+    def comb(c, n=256, z=A, lse=None):
+        return lib.mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n, A, A, z, lse, None)
+
+    assert dec(_cache(), n=0) == M.MLA_ERR_SHAPE
+    assert dec(_cache(), n=M.MLA_BALANCED_MAX_UNITS + 1) == M.MLA_ERR_UNSUPPORTED
+    assert dec(_cache(), q=None) == M.MLA_ERR_NULL
+    assert dec(_cache(), o=U) == M.MLA_ERR_ALIGN
+    assert dec(_cache(seq_lens=0)) == M.MLA_ERR_NULL
+    assert dec(_cache(batch=0)) == M.MLA_OK
+    # device-side cost sums must stay inside int32
+    assert dec(_cache(batch=65535, max_pages=1 << 16, page_size=64)) == M.MLA_ERR_UNSUPPORTED
+    assert comb(_cache(), n=0) == M.MLA_ERR_SHAPE
+    assert comb(_cache(), z=None) == M.MLA_ERR_NULL
+    assert comb(_cache(), lse=U) == M.MLA_ERR_ALIGN
+    assert comb(_cache(batch=0)) == M.MLA_OK

@@ -163,3 +163,135 @@ def test_split_invariance():
     for z, lse in zs[1:]:
         assert np.max(np.abs(z - zs[0][0])) <= 2e-2 * np.sqrt(np.mean(zs[0][0] ** 2))
         assert np.max(np.abs(lse - zs[0][1])) <= 1e-3
+
+
+# ------------------------------------------------------------------------------ balanced split
+from balanced_ref import segments  # noqa: E402
+
+
+def _run_balanced(inp, n_units, q_hat_np=None, flags=0):
+    st = runner.DecodeStep(inp, 0, DEV, flags=flags, n_units=n_units)
+    if q_hat_np is None:
+        st.absorb()
+    else:
+        st.q_hat.copy_(runner.to_device(q_hat_np, DEV))
+    st.attend()
+    st.combine()
+    torch.cuda.synchronize()
+    return st
+
+
+def _segment_parts(st, lens):
+    """Partials of the non-empty segments only (other slots are never written)."""
+    segs = segments(lens, st.n_units)
+    idx = [s[4] for s in segs]
+    return _np(st.o_part)[idx].copy(), _np(st.lse_part)[idx].copy()
+
+
+BAL_LENS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 500, 1000, 1024, 1025, 0, 3000, 31, 33]
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("n_units", [1, 3, 16, 64, 256, 2048])
+def test_count_balanced(n_units, flags):
+    lens = BAL_LENS
+    note(f"count balanced n_units={n_units} flags={flags}")
+    inp = gen.make_decode_inputs(_w(len(lens)), lens=np.array(lens, np.int32), fill="nan")
+    q0 = np.zeros((len(lens), 128, 576), np.uint16)
+    st = _run_balanced(inp, n_units, q0, flags=flags)
+    lse_p = _np(st.lse_part)
+    segs = segments(lens, n_units)
+    assert segs and len({s[4] for s in segs}) == len(segs)
+    for w, b, t0, t1, slot in segs:
+        e = np.exp(lse_p[slot].astype(np.float64))
+        assert np.all(np.rint(e) == t1 - t0), (w, b, t0, t1, e[:4])
+    lse = _np(st.lse).astype(np.float64)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(lse[b] == -np.inf) and np.all(_np(st.z)[b] == 0)
+        else:
+            assert np.all(np.rint(np.exp(lse[b])) == L), b
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("n_units", [1, 5, 256])
+def test_spike_balanced(n_units, flags):
+    cases = []
+    for L in (1, 65, 1000, 1025):
+        cases += [(L, t) for t in sorted({0, 31, 32, L // 2, L - 1}) if t < L]
+    note(f"spike balanced n_units={n_units} flags={flags} cases={len(cases)}")
+    inp, q, rows = _spike_inputs(cases)
+    st = _run_balanced(inp, n_units, q, flags=flags)
+    z, lse = _np(st.z), _np(st.lse)
+    for b, (L, t) in enumerate(cases):
+        want = gen.bf16_from_bits(rows[b][t, :512]).astype(np.float64)
+        err = np.max(np.abs(z[b] - want[None]))
+        assert err <= 1e-5, f"len {L} spike {t}: z off by {err}"
+        assert np.allclose(lse[b], 128.0 * np.log(2.0), atol=1e-4), (L, t, lse[b, :2])
+
+
+def test_long_segment_page_windows():
+    """Segments longer than 64 pages move the page-id window inside the tile loop; with a spike
+    near the end the rerun pass restarts from the first window.  Page size 32 (one tile per
+    page) makes 64 pages only 2,048 tokens."""
+    L = 5000
+    cases = [(L, L - 1), (L, 2100), (L, 2047), (L, 2048)]
+    note("long segment windows")
+    rng = np.random.default_rng(5)
+    rows = []
+    for _, t in cases:
+        c = rng.standard_normal((L, 576)).astype(np.float32)
+        c[:, 0] = 0.0
+        c[t, 0] = 8.0
+        rows.append(gen.bf16_bits(c))
+    w = gen.Workload(name="exact", seed=5, kind="decode", batch=len(cases), random_pages=True, page_size=32, **V3)
+    inp = gen.make_decode_inputs(w, lens=np.full(len(cases), L, np.int32), latent_rows=rows, fill="nan")
+    q = np.zeros((len(cases), 128, 576), np.float32)
+    q[:, :, 0] = 16.0
+    qb = gen.bf16_bits(q)
+    for mode in ("balanced", "fixed"):
+        if mode == "balanced":
+            st = _run_balanced(inp, 1, qb)
+        else:
+            st = _run_partial(inp, 8192, qb)
+        assert st.uses_mfma()
+        z = _np(st.z)
+        for b, (_, t) in enumerate(cases):
+            want = gen.bf16_from_bits(rows[b][t, :512]).astype(np.float64)
+            assert np.max(np.abs(z[b] - want[None])) <= 1e-5, (mode, t)
+    # counts over the same long segments with a zero query
+    st = _run_balanced(inp, 1, np.zeros_like(qb))
+    assert np.all(np.rint(np.exp(_np(st.lse).astype(np.float64))) == L)
+
+
+@pytest.mark.parametrize("flags", PATHS)
+def test_poison_bitwise_balanced(flags):
+    lens = np.array([1, 63, 64, 65, 700, 1234, 4000, 0], np.int32)
+    note(f"poison balanced flags={flags}")
+    outs = []
+    for fill in ("zero", "nan", "inf"):
+        inp = gen.make_decode_inputs(_w(len(lens)), lens=lens, fill=fill, spare_pages=16)
+        st = _run_balanced(inp, 7, flags=flags)
+        st.out_proj()
+        torch.cuda.synchronize()
+        outs.append(list(_segment_parts(st, lens)) + [_np(x).copy() for x in (st.z, st.lse, st.out)])
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_balanced_matches_fixed_and_is_deterministic():
+    lens = np.array([3000, 70, 4096, 1, 999], np.int32)
+    note("balanced vs fixed")
+    inp = gen.make_decode_inputs(_w(len(lens), seed=43), lens=lens)
+    ref = _run_partial(inp, 4096)
+    z0 = _np(ref.z).copy()
+    for n_units in (1, 4, 33, 256):
+        st = _run_balanced(inp, n_units)
+        z, lse = _np(st.z).copy(), _np(st.lse).copy()
+        assert np.max(np.abs(z - z0)) <= 2e-2 * np.sqrt(np.mean(z0 ** 2)), n_units
+        assert np.max(np.abs(lse - _np(ref.lse))) <= 1e-3
+        st.attend()
+        st.combine()
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(st.z).view(np.uint32), z.view(np.uint32)), "re-run differs"

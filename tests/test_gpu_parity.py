@@ -15,6 +15,7 @@ import mla_latent_kv_31_amd as M
 import oracle.mla_oracle as O
 from mla_latent_kv_31_amd import runner
 from mla_workloads import gen
+from balanced_ref import segments
 from parity import TOL, OracleView, assert_abs_close, assert_mid_close, assert_rms_close, note
 
 pytestmark = pytest.mark.gpu
@@ -118,10 +119,38 @@ def inp_ragged():
     return gen.make_decode_inputs(gen.WORKLOADS["v3_b64_ragged_paged"])
 
 
-def test_v3_b64_ragged_paged_sampled(inp_ragged):
+def _decode_step(inp, mode, flags=0):
+    """The fixed split at the workload's chunk length, or the balanced split over the device's
+    compute units (the configuration the benchmark times)."""
+    w = inp["workload"]
+    if mode == "balanced":
+        n = runner.balanced_units(inp["lens"], runner.compute_units(DEV))
+        return runner.DecodeStep(inp, 0, DEV, flags=flags, n_units=n)
+    split = w.split_tokens if mode == "fixed" else int(mode)
+    return runner.DecodeStep(inp, split, DEV, flags=flags)
+
+
+def _check_balanced_slots(st, view, picks, heads):
+    """Compare the partials of a few balanced segments with the oracle over their token ranges."""
+    segs = segments(_lens_of(st), st.n_units)
+    for k in picks:
+        w_, b, t0, t1, slot = segs[k % len(segs)]
+        r = view.decode(b, heads=heads, key_range=(t0, t1))
+        assert_mid_close(_np(st.o_part)[slot, heads], r["z"][heads], "bf16", f"o_part slot {slot} seq {b} [{t0},{t1})")
+        assert_abs_close(_np(st.lse_part)[slot, heads], r["lse"][heads], TOL["bf16"], f"lse_part slot {slot}")
+
+
+def _lens_of(st):
+    return st.lens.cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", ["fixed", "balanced"])
+def test_v3_b64_ragged_paged_sampled(inp_ragged, mode):
     w = inp_ragged["workload"]
-    note(f"v3_b64_ragged_paged split={w.split_tokens} total_tokens={int(inp_ragged['lens'].sum())}")
-    st = runner.DecodeStep(inp_ragged, w.split_tokens, DEV)
+    st = _decode_step(inp_ragged, mode)
+    note(f"v3_b64_ragged_paged mode={mode} split={st.split_tokens} units={st.n_units} "
+         f"total_tokens={int(inp_ragged['lens'].sum())}")
+    assert st.uses_mfma()
     st.run()
     torch.cuda.synchronize()
     view = OracleView(inp_ragged)
@@ -134,6 +163,8 @@ def test_v3_b64_ragged_paged_sampled(inp_ragged):
         assert_mid_close(_np(st.z)[b, heads], ref["z"][heads], "bf16", f"z seq {b}")
         assert_abs_close(_np(st.lse)[b, heads], ref["lse"][heads], tol, f"lse seq {b}")
         assert_rms_close(_np(st.out)[b, heads], ref["o"][heads], tol, f"o seq {b}")
+    if mode == "balanced":
+        _check_balanced_slots(st, view, (0, 1, 150, -1), [3, 100])
     # any-size properties on every output: finite, and z inside the convex hull bound of |c|
     assert np.isfinite(_np(st.out)).all() and np.isfinite(_np(st.lse)).all()
 
@@ -143,11 +174,15 @@ def inp_long():
     return gen.make_decode_inputs(gen.WORKLOADS["v3_b4_ctx128k"])
 
 
-def test_v3_b4_ctx128k_sampled(inp_long):
-    w = inp_long["workload"]
-    note(f"v3_b4_ctx128k split={w.split_tokens}")
-    st = runner.DecodeStep(inp_long, w.split_tokens, DEV)
-    assert st.S >= 256
+@pytest.mark.parametrize("mode", ["fixed", "512", "balanced"])
+def test_v3_b4_ctx128k_sampled(inp_long, mode):
+    st = _decode_step(inp_long, mode)
+    note(f"v3_b4_ctx128k mode={mode} split={st.split_tokens} units={st.n_units}")
+    if st.n_units is None:
+        assert st.B * st.S >= 256  # at least 256 split-K chunks over the batch
+    else:
+        assert len(segments(_lens_of(st), st.n_units)) >= 256
+    assert st.uses_mfma()
     st.run()
     torch.cuda.synchronize()
     view = OracleView(inp_long)
@@ -157,7 +192,10 @@ def test_v3_b4_ctx128k_sampled(inp_long):
         assert_mid_close(_np(st.z)[b, h], ref["z"][h], "bf16", f"z ({b},{h})")
         assert_abs_close(_np(st.lse)[b, h], ref["lse"][h], tol, f"lse ({b},{h})")
         assert_rms_close(_np(st.out)[b, h], ref["o"][h], tol, f"o ({b},{h})")
-    for i in (0, 1, 128, st.S - 1):
+    if st.n_units is not None:
+        _check_balanced_slots(st, view, (0, 1, 128, -1), [5])
+        return
+    for i in (0, 1, st.S // 2, st.S - 1):
         r = view.decode(1, heads=[5], key_range=(i * st.split_tokens, (i + 1) * st.split_tokens))
         assert_mid_close(_np(st.o_part)[1, i, 5], r["z"][5], "bf16", f"o_part chunk {i}")
         assert_abs_close(_np(st.lse_part)[1, i, 5], r["lse"][5], tol, f"lse_part chunk {i}")
@@ -194,12 +232,15 @@ def _small(dtype, lens, seed=11, random_pages=True, H=128):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("split", [64, 192, 4096])
+@pytest.mark.parametrize("split", [64, 192, 4096, "units=1", "units=7", "units=256"])
 def test_v3_small_ragged_all_heads(dtype, split):
     lens = [1, 63, 64, 65, 300, 1000]
     note(f"small ragged dtype={dtype} split={split}")
     inp = _small(dtype, lens)
-    st = runner.DecodeStep(inp, split, DEV)
+    if isinstance(split, str):
+        st = runner.DecodeStep(inp, 0, DEV, n_units=int(split.split("=")[1]))
+    else:
+        st = runner.DecodeStep(inp, split, DEV)
     st.run()
     torch.cuda.synchronize()
     view = OracleView(inp)
