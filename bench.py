@@ -102,18 +102,144 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
                       f"unabsorbed fp64 NumPy) in {el:.1f} s"}
 
 
+def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle on prefill rows of the same workload until `seconds` pass (algorithmic flops/s)."""
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = inp["dtype"]
+    w_uk = gen.as_f64(inp["w_uk"], dt)
+    w_uv = gen.as_f64(inp["w_uv"], dt)
+    flops, n = 0, 0
+    t0 = time.perf_counter()
+    b = 0
+    cache = gen.as_f64(O.gather_rows(inp["pool"], inp["page_table"], b, int(inp["lens"][b])), dt)
+    for i in range(w.q_len):
+        p = int(inp["q_start"][b]) + i
+        O.attention(gen.as_f64(inp["q_c"][b, i], dt), gen.as_f64(inp["q_r"][b, i], dt), p, cache[:p + 1], w_uk, w_uv,
+                    w.d_c, base=w.rope_base)
+        flops += (p + 1) * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 9), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.q_len} query rows of sequence 0 (all {w.n_heads} heads, unabsorbed fp64 "
+                      f"NumPy; algorithmic absorbed flops counted) in {el:.1f} s"}
+
+
+def bench_prefill(args, w) -> dict:
+    """Chunked prefill: absorb -> mla_prefill_chunk -> out_proj per step; MFMA-bound."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    inp = gen.make_prefill_inputs(w)
+    dev = torch.device("cuda:0")
+    st = runner.PrefillStep(inp, dev)
+    pairs = int(sum(min(int(inp["lens"][b]), int(inp["q_start"][b]) + i + 1)
+                    for b in range(w.batch) for i in range(w.q_len)))
+    flops_attn = pairs * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+    flops_proj = w.batch * w.q_len * 2 * w.n_heads * w.d_c * (w.d_k + w.d_v)
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        st.absorb()
+        ev[i][0].record(stream)
+        st.attend()
+        ev[i][1].record(stream)
+        st.out_proj()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    ms_attn = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tf_attn = flops_attn / (ms_attn * 1e-3) / 1e12
+    rec = {
+        "metric": "MLA chunked-prefill TFLOP/s (V3 shape, 1 GPU)",
+        "value": round((flops_attn + flops_proj) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prior_tokens": w.ctx, "chunk": w.q_len,
+                   "heads": w.n_heads, "d_c": w.d_c, "d_r": w.d_r, "causal_pairs": pairs, "seed": w.seed,
+                   "prefill_kernel": "mfma" if st.uses_mfma() else "generic"},
+        "query_tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "mla_prefill_chunk", "achieved": round(tf_attn, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_attn, 6), "algorithmic_flops_per_launch": flops_attn},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    return rec
+
+
+COPY_PROBE_KERNEL = "neg_kernel"  # the calibration copy: torch.neg over a float32 buffer (1 read, 1 write)
+
+
+def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, copy_mb: int) -> dict:
+    """HBM bytes per decode launch from two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch), each scaled by what the same counter reads for the plain
+    copy of --copy-probe-mb MiB that the profiled runs launched first."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    out = {"workload": workload, "kernel_source_sha": _kernel_sha(), "copy_probe_bytes": copy_mb << 20}
+    for counter, path, tag in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
+        v = per_kernel(path, counter)
+        copy = [x for (k, _), x in v.items() if COPY_PROBE_KERNEL in k]
+        dec = [x for (k, _), x in v.items() if "decode_mfma" in k]
+        if not copy or not dec:
+            raise SystemExit(f"{path}: copy probe or decode kernel missing")
+        factor = (copy_mb << 20) / (max(copy) * 1024.0)  # the probe moves copy_mb MiB each way
+        out[f"{tag}_factor"] = round(factor, 4)
+        out[f"{tag}_bytes_per_launch"] = round(statistics.median(dec) * 1024.0 * factor)
+    out["hbm_bytes_per_launch"] = out["read_bytes_per_launch"] + out["write_bytes_per_launch"]
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The warm-up runs long enough (~0.1 s) for the clocks to settle at their sustained level
+    # under the board power limit; shorter runs time a ramping clock.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--split-tokens", type=int, default=None,
                     help="fixed split-K chunks of this many tokens instead of the balanced split")
     ap.add_argument("--units", type=int, default=None, help="units of the balanced split (default: one per CU)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="launch one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/decode_traffic_<workload>.json from two rocprofv3 --pmc runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        rec = traffic_from_counters(args.workload, args.traffic_from[0], args.traffic_from[1], args.copy_probe_mb)
+        with open(os.path.join(ROOT, "profiles", f"decode_traffic_{args.workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -128,11 +254,20 @@ def main() -> int:
     from mla_workloads import gen
 
     w = gen.WORKLOADS[args.workload]
+    if w.kind == "prefill":
+        print(json.dumps(bench_prefill(args, w)), flush=True)
+        return 0
     if w.kind != "decode":
-        print(f"workload {w.name} is not a decode workload", file=sys.stderr)
+        print(f"workload {w.name} is neither a decode nor a prefill workload", file=sys.stderr)
         return 2
     inp = gen.make_decode_inputs(w)
     dev = torch.device("cuda:0")
+    if args.copy_probe_mb:  # a plain streaming copy of known size, for counter calibration
+        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if args.split_tokens:
         st = runner.DecodeStep(inp, args.split_tokens, dev)
     else:

@@ -108,9 +108,11 @@ int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32
 }
 
 int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache) {
-  (void)dims;
-  (void)cache;
-  return 0;
+  Dims d;
+  Cache c;
+  if (check_dims(dims, &d) != MLA_OK || check_cache(cache, &c) != MLA_OK) return 0;
+  if (dims->flags & MLA_FLAG_FORCE_GENERIC) return 0;
+  return prefill_mfma_supported(d, c) ? 1 : 0;
 }
 
 mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q_r, const void* w_uk,
@@ -228,6 +230,9 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
   if (c.batch == 0 || q_len == 0) return MLA_OK;
+  if (int64_t(c.batch) * q_len > (int64_t(1) << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && prefill_mfma_supported(d, c))
+    return hip_status(launch_prefill_mfma(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream));
   return hip_status(launch_prefill_generic(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream));
 }
 

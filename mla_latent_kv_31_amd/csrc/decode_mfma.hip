@@ -124,15 +124,22 @@ __device__ __forceinline__ int load_page_window(const int32_t* row, int first, i
   return lane < count ? v : 0;
 }
 
-// One workgroup runs a list of segments (sequence, token range, partial slot): one chunk of the
-// fixed split (grid = chunks x sequences), or every segment of one unit of the balanced split
-// (grid = units; see schedule.h).
-template <bool kBalanced>
+// What a workgroup runs: a list of segments (query row, sequence, token range, output row).
+enum Mode {
+  kFixed = 0,     // one chunk of the fixed split; grid = chunks x sequences
+  kBalanced = 1,  // every segment of one unit of the balanced split; grid = units (schedule.h)
+  kPrefill = 2,   // one query row of a prefill chunk over its whole causal key range, written
+                  // straight to z / lse; grid = rows, longest rows first
+};
+
+template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __restrict__ page_table,
                         const int32_t* __restrict__ seq_lens, int batch, int max_pages, int page_size,
                         int tiles_per_page_log2, const uint16_t* __restrict__ q_hat, int n_splits,
-                        int split_tokens, float* __restrict__ o_part, float* __restrict__ lse_part) {
+                        int split_tokens, const int32_t* __restrict__ q_start, float* __restrict__ o_part,
+                        float* __restrict__ lse_part) {
+  constexpr bool kBal = MODE == kBalanced;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kNBuf * kTileB + kH * kRopeB];  // 160 KiB
   lds_u8* const lbase = (lds_u8*)smem;
 
@@ -191,7 +198,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
   // ---- the segment list
   const int unit = blockIdx.x;
   int next_b, next_cb = 0, unit_end = 0, quota = 0;
-  if constexpr (kBalanced) {
+  if constexpr (kBal) {
     int total;
     sched_prefix(seq_lens, batch, cap, 0, next_cb, total);
     total = __builtin_amdgcn_readfirstlane(total);  // wave-uniform: keep the segment loop scalar
@@ -207,8 +214,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
 
   for (bool first_seg = true;; first_seg = false) {
     int b, t0, t1;
-    size_t slot;
-    if constexpr (kBalanced) {
+    size_t slot, qrow;  // output row group and q_hat row group (128 heads each)
+    if constexpr (kBal) {
       if (next_b >= batch || next_cb >= unit_end) break;
       b = next_b;
       const int len = sched_len(seq_lens[b], cap);
@@ -220,8 +227,23 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       t0 = k0 * kTile;
       t1 = min(k1 * kTile, len);
       slot = size_t(unit) + b;
+      qrow = b;
+    } else if constexpr (MODE == kPrefill) {
+      // n_splits carries the chunk length; row i of sequence b reads keys t <= q_start[b] + i
+      const int i = n_splits - 1 - unit / batch;
+      b = unit % batch;
+      qrow = slot = size_t(b) * n_splits + i;
+      t0 = 0;
+      t1 = min(sched_len(seq_lens[b], cap), max(q_start[b] + i + 1, 0));
+      if (t1 <= 0) {  // no visible key: z = 0, lse = -inf
+        float* zr = o_part + (slot * kH + head) * kDc + 4 * hi;
+        for (int c = 0; c < kDc; c += 8) *reinterpret_cast<float4*>(zr + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hi == 0 && lse_part) lse_part[slot * kH + head] = -INFINITY;
+        return;
+      }
     } else {
       b = next_b;
+      qrow = b;
       t0 = unit * split_tokens;
       t1 = min(t0 + split_tokens, sched_len(seq_lens[b], cap));
       slot = size_t(b) * n_splits + unit;
@@ -269,10 +291,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     // tile's rotary rows), which keeps the register file within budget.
     bf16x8 qf[kKLat];
     {
-      const uint16_t* qrow = q_hat + (size_t(b) * kH + head) * kW + 8 * hi;
+      const uint16_t* qp = q_hat + (qrow * kH + head) * kW + 8 * hi;
 #pragma unroll
-      for (int k = 0; k < kKLat; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qrow + 16 * k);
-      const uint16_t* qb = q_hat + size_t(b) * kH * kW + kDc;
+      for (int k = 0; k < kKLat; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+      const uint16_t* qb = q_hat + qrow * kH * kW + kDc;
 #pragma unroll
       for (int x = 0; x < kH * kRopeB / 16 / kThreads; ++x) {  // 4 chunks of 16 B per thread
         const int c = threadIdx.x + x * kThreads, h = c >> 3, ch = c & 7;
@@ -350,55 +372,79 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         const unsigned char* gnext = tile_src(dma_next ? j + 2 : j);  // never look past the segment
         const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
 
-        // ---- scores of tile j interleaved with the weighted sum of tile j-1
+        // ---- phase A: scores of tile j, one dependent MFMA chain, operands read three steps
+        // ahead; the nine transfers of tile j+2 are spread over it
         f32x16 sacc;
 #pragma unroll
         for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
-        bf16x8 qa[3], pa[3], qb[3];  // operands loaded two steps ahead (qb: rotary q_hat steps)
-        auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
-        qa[0] = lds16(a_src(tb, 0));
-        pa[0] = tr8(tp, 0);
-        qa[1] = lds16(a_src(tb, 1));
-        pa[1] = tr8(tp, 1);
+        {
+          bf16x8 qa[4], qb[4];  // qb: rotary q_hat steps
+          auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
 #pragma unroll
-        for (int i = 0; i < kKSteps; ++i) {
-          if (i + 2 < kKSteps) {
-            qa[(i + 2) % 3] = lds16(a_src(tb, i + 2));
-            if (i + 2 >= kKLat) qb[(i + 2) % 3] = lds16(b_src(i + 2));
+          for (int i = 0; i < 3; ++i) qa[i] = lds16(a_src(tb, i));
+#pragma unroll
+          for (int i = 0; i < kKSteps; ++i) {
+            if (i + 3 < kKSteps) {
+              qa[(i + 3) % 4] = lds16(a_src(tb, i + 3));
+              if (i + 3 >= kKLat) qb[(i + 3) % 4] = lds16(b_src(i + 3));
+            }
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % 4], i < kKLat ? qf[i] : qb[i % 4], sacc, 0, 0, 0);
+            if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % 3], i < kKLat ? qf[i] : qb[i % 3], sacc, 0, 0, 0);
-          if (i < kPvSteps) {
-            if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
-            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15],
-                                                                  0, 0, 0);
-          }
-          if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);  // nine transfers of tile j+2
-          __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- online softmax of tile j (base-2 logits); lane = one head, lanes (l, l^32) share it
-        if (nvalid < kTile) {
+        // ---- phase B: weighted sum of tile j-1 (32 independent MFMAs) with the online softmax of
+        // tile j (base-2 logits; lane = one head, lanes l and l^32 share it) woven between them,
+        // so the VALU work runs in the shadow of the matrix cores.  Branch-free: the tail mask
+        // and the reference update are selects.
+        {
+          bf16x8 pa[4];
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
-            if (tok >= nvalid) sacc[x] = -INFINITY;
+          for (int i = 0; i < 3; ++i) pa[i] = tr8(tp, i);
+          const bool first = pass == 0 && j == 0;  // the segment's first tile fixes the reference
+          float mx0 = 0.f, mx = 0.f, pr[16];
+          bf16x8 pn0, pn1;
+#pragma unroll
+          for (int i = 0; i < kPvSteps; ++i) {
+            if (i + 3 < kPvSteps) pa[(i + 3) % 4] = tr8(tp, i + 3);
+            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 4], (i < kMBlk) ? pb0 : pb1, acc[i & 15],
+                                                                  0, 0, 0);
+            if (i == 1 || i == 2) {  // tail mask and row maximum, one half per step
+              float m = -INFINITY;
+#pragma unroll
+              for (int x = 8 * (i - 1); x < 8 * i; ++x) {
+                const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
+                sacc[x] = tok < nvalid ? sacc[x] : -INFINITY;
+                m = fmaxf(m, sacc[x]);
+              }
+              if (i == 1) {
+                mx0 = m;
+              } else {
+                mx = lane_swap_max(fmaxf(mx0, m));
+                m_ref = first ? mx : m_ref;
+                m_max = fmaxf(m_max, mx);
+                over |= mx > m_ref + kRerunMargin;
+              }
+            } else if (i >= 3 && i < 11) {  // two probabilities per step
+              const int x = 2 * (i - 3);
+              pr[x] = fast_exp2(sacc[x] - m_ref);
+              pr[x + 1] = fast_exp2(sacc[x + 1] - m_ref);
+            } else if (i == 11) {
+              float t = 0.f;
+#pragma unroll
+              for (int x = 0; x < 16; ++x) t += pr[x];
+              l_lane += t;
+            } else if (i == 12) {
+              pn0 = pack8(&pr[0]);
+            } else if (i == 13) {
+              pn1 = pack8(&pr[8]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
+          pb0 = pn0;
+          pb1 = pn1;
         }
-        float mx = sacc[0];
-#pragma unroll
-        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
-        mx = lane_swap_max(mx);
-        if (pass == 0 && j == 0) m_ref = mx;  // the segment's first tile fixes the reference
-        m_max = fmaxf(m_max, mx);
-        over |= mx > m_ref + kRerunMargin;
-        float pr[16];
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          pr[x] = fast_exp2(sacc[x] - m_ref);
-          l_lane += pr[x];
-        }
-        pb0 = pack8(&pr[0]);
-        pb1 = pack8(&pr[8]);
       }
 
       // ---- weighted sum of the last tile
@@ -440,8 +486,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         *reinterpret_cast<float4*>(op + 32 * mb + 8 * j4) = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (hi == 0) lse_part[orow] = (m_ref + log2f(l_tot)) * kLn2;
-    if constexpr (!kBalanced) break;
+    if (hi == 0 && lse_part) lse_part[orow] = (m_ref + log2f(l_tot)) * kLn2;
+    if constexpr (!kBal) break;
   }
 }
 
@@ -457,9 +503,9 @@ hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, 
                               float* o_part, float* lse_part, hipStream_t s) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<false><<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
+  decode_mfma_kernel<kFixed><<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
-      static_cast<const uint16_t*>(q_hat), n_splits, split_tokens, o_part, lse_part);
+      static_cast<const uint16_t*>(q_hat), n_splits, split_tokens, nullptr, o_part, lse_part);
   return hipGetLastError();
 }
 
@@ -467,9 +513,21 @@ hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void
                                        float* lse_part, hipStream_t s) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<true><<<dim3(n_units), kThreads, 0, s>>>(
+  decode_mfma_kernel<kBalanced><<<dim3(n_units), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
-      static_cast<const uint16_t*>(q_hat), n_units, 0, o_part, lse_part);
+      static_cast<const uint16_t*>(q_hat), n_units, 0, nullptr, o_part, lse_part);
+  return hipGetLastError();
+}
+
+bool prefill_mfma_supported(const Dims& d, const Cache& c) { return decode_mfma_supported(d, c, 0); }
+
+hipError_t launch_prefill_mfma(const Dims& d, const Cache& c, const void* q_hat, int q_len, const int32_t* q_start,
+                               float* z, float* lse, hipStream_t s) {
+  (void)d;
+  const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
+  decode_mfma_kernel<kPrefill><<<dim3(c.batch * q_len), kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
+      static_cast<const uint16_t*>(q_hat), q_len, 0, q_start, z, lse);
   return hipGetLastError();
 }
 

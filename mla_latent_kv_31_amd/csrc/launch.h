@@ -35,6 +35,10 @@ hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, 
                               float* o_part, float* lse_part, hipStream_t s);
 hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
                                        float* lse_part, hipStream_t s);
+// chunked prefill on the same kernel: one workgroup per query row over its causal key range
+bool prefill_mfma_supported(const Dims& d, const Cache& c);
+hipError_t launch_prefill_mfma(const Dims& d, const Cache& c, const void* q_hat, int q_len, const int32_t* q_start,
+                               float* z, float* lse, hipStream_t s);
 
 // ---- bf16 MFMA per-head projections (d_c 512, d_k = d_v = 128) and the vectorised combine
 bool proj_mfma_supported(const Dims& d);

@@ -295,3 +295,62 @@ def test_balanced_matches_fixed_and_is_deterministic():
         st.combine()
         torch.cuda.synchronize()
         assert np.array_equal(_np(st.z).view(np.uint32), z.view(np.uint32)), "re-run differs"
+
+
+# ------------------------------------------------------------------------------ prefill causal mask
+def _prefill_direct(inp, q_hat_np, q_start, flags=0):
+    """mla_prefill_chunk on a given q_hat [B, q_len, H, 576] (bf16 bits) and q_start [B]."""
+    w = inp["workload"]
+    d = runner.dims_for(w, flags)
+    pool = runner.to_device(inp["pool"], DEV)
+    table = runner.to_device(inp["page_table"], DEV)
+    lens = runner.to_device(inp["lens"].astype(np.int32), DEV)
+    c = M.cache(pool, table, lens)
+    qh = runner.to_device(q_hat_np, DEV)
+    B, Sq = q_hat_np.shape[:2]
+    z = torch.empty((B, Sq, 128, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, Sq, 128), dtype=torch.float32, device=DEV)
+    M.mla_prefill_chunk(d, c, qh, Sq, runner.to_device(np.asarray(q_start, np.int32), DEV), z, lse)
+    torch.cuda.synchronize()
+    return _np(z), _np(lse), M.mla_prefill_uses_mfma(d, c)
+
+
+@pytest.mark.parametrize("flags", PATHS)
+def test_prefill_count_and_causal_spike(flags):
+    """Zero query: lse = ln(visible keys) for every row.  Spike at token T (logit 128): rows at
+    positions >= T return exactly that latent, rows before it never see it."""
+    lens = np.array([300, 97], np.int32)
+    T = 150
+    Sq = 40
+    q_start = np.array([130, 57], np.int32)  # seq 0 rows 130..169 straddle T; seq 1 rows 57..96
+    rng = np.random.default_rng(7)
+    rows = []
+    for L in lens:
+        cr = rng.standard_normal((L, 576)).astype(np.float32)
+        cr[:, 0] = 0.0
+        rows.append(cr)
+    rows[0][T, 0] = 8.0
+    rows = [gen.bf16_bits(r) for r in rows]
+    inp = gen.make_decode_inputs(_w(2, seed=8), lens=lens, latent_rows=rows, fill="nan")
+    note(f"prefill count/spike flags={flags}")
+    # count
+    z, lse, mf = _prefill_direct(inp, np.zeros((2, Sq, 128, 576), np.uint16), q_start, flags)
+    assert mf == (flags == 0)
+    for b in range(2):
+        for i in range(Sq):
+            vis = min(int(lens[b]), int(q_start[b]) + i + 1)
+            assert np.all(np.rint(np.exp(lse[b, i].astype(np.float64))) == vis), (b, i, vis)
+    # spike
+    q = np.zeros((2, Sq, 128, 576), np.float32)
+    q[..., 0] = 16.0
+    z, lse, _ = _prefill_direct(inp, gen.bf16_bits(q), q_start, flags)
+    spike = gen.bf16_from_bits(rows[0][T, :512]).astype(np.float64)
+    for i in range(Sq):
+        p = int(q_start[0]) + i
+        if p >= T:
+            assert np.max(np.abs(z[0, i] - spike[None])) <= 1e-5, i
+            assert np.allclose(lse[0, i], 128.0 * np.log(2.0), atol=1e-4), i
+        else:
+            assert np.all(np.rint(np.exp(lse[0, i].astype(np.float64))) == p + 1), i
+    for i in range(Sq):
+        assert np.all(np.rint(np.exp(lse[1, i].astype(np.float64))) == min(97, 57 + i + 1))

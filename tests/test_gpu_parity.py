@@ -211,6 +211,7 @@ def inp_prefill():
 def test_v3_prefill_sampled(inp_prefill, flags):
     note(f"v3_prefill_b2 flags={flags}")
     st = runner.PrefillStep(inp_prefill, DEV, flags=flags)
+    assert st.uses_mfma() == (flags == 0)
     st.run()
     torch.cuda.synchronize()
     view = OracleView(inp_prefill)
@@ -218,6 +219,29 @@ def test_v3_prefill_sampled(inp_prefill, flags):
     heads = [0, 64, 127]
     for b in (0, 1):
         for i in (0, 1, 63, 64, 255, 510, 511):
+            ref = view.prefill_row(b, i, heads)
+            assert_mid_close(_np(st.z)[b, i, heads], ref["z"][heads], "bf16", f"z ({b},{i})")
+            assert_abs_close(_np(st.lse)[b, i, heads], ref["lse"][heads], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i, heads], ref["o"][heads], tol, f"o ({b},{i})")
+
+
+@pytest.mark.parametrize("flags", [0, M.MLA_FLAG_FORCE_GENERIC])
+def test_prefill_small_ragged_start_all_rows(flags):
+    """Small chunks with different starts per sequence (q_start 0 puts the first row on a single
+    key); every row of every sequence on three heads, z / lse / o against the oracle."""
+    w = gen.Workload(name="prefill_small", seed=9, kind="prefill", batch=3, ctx=70, q_len=40, random_pages=True)
+    inp = gen.make_prefill_inputs(w)
+    inp["q_start"] = np.array([70, 0, 33], np.int32)  # rows past q_start+i stay invisible
+    note(f"prefill small flags={flags}")
+    st = runner.PrefillStep(inp, DEV, flags=flags)
+    assert st.uses_mfma() == (flags == 0)
+    st.run()
+    torch.cuda.synchronize()
+    view = OracleView(inp)
+    heads = [0, 61, 127]
+    tol = TOL["bf16"]
+    for b in range(3):
+        for i in range(40):
             ref = view.prefill_row(b, i, heads)
             assert_mid_close(_np(st.z)[b, i, heads], ref["z"][heads], "bf16", f"z ({b},{i})")
             assert_abs_close(_np(st.lse)[b, i, heads], ref["lse"][heads], tol, f"lse ({b},{i})")
