@@ -126,7 +126,7 @@ mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q
   MLA_TRY(ptr_ok(pos));
   MLA_TRY(ptr_ok(q_hat));
   if (rows == 0) return MLA_OK;
-  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && proj_mfma_supported(d))
+  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && proj_mfma_supported(d) && rows <= 65535 * 64)
     return hip_status(launch_absorb_mfma(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
   return hip_status(launch_absorb_generic(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
 }
