@@ -39,11 +39,18 @@ DECODE_SOURCES = ("mla_latent_kv_31_amd/csrc/decode_mfma.hip", "mla_latent_kv_31
 
 
 def _kernel_sha() -> str:
+    """Hash of the decode kernel's sources with comments and blank space removed, so that stored
+    counter results stay tied to the code they measured and nothing else."""
+    import re
+
     h = hashlib.sha256()
     for rel in DECODE_SOURCES:
         p = os.path.join(ROOT, rel)
         if os.path.exists(p):
-            h.update(open(p, "rb").read())
+            text = open(p, encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            h.update(re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()[:16]
 
 

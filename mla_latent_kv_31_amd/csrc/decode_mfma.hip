@@ -1,26 +1,29 @@
 // Split-K flash-decode over the latent cache on bf16 MFMA (gfx950), DeepSeek-V3 shape:
 // 128 heads, rows of 576 values = [c^KV (512) | k^R (64)], bf16 cache and q_hat, fp32 accumulate.
+// The same kernel runs chunked prefill: a prefill query row is a decode query with its own causal
+// key range.
 //
-// One workgroup per (chunk, sequence); four waves, wave w owns heads 32w..32w+31 for the whole
-// chunk.  All 128 heads read the same cached rows, so each 32-token tile (36,864 B) is fetched
-// from HBM once per workgroup, straight into LDS with 16-byte global_load_lds transfers.  Four
-// LDS buffers rotate: tile j is being scored, tile j-1 is being summed, tiles j+1 and j+2 are
-// streaming in.
+// A workgroup runs a list of segments (query row, sequence, token range, output row): one chunk
+// of the fixed split, all segments of one unit of the work-balanced split (schedule.h), or one
+// prefill row.  Four waves; wave w owns heads 32w..32w+31 for the whole segment.  All 128 heads
+// read the same cached rows, so each 32-token tile (36,864 B) is fetched from HBM once per
+// workgroup, straight into LDS with 16-byte global_load_lds transfers.  Four LDS buffers rotate:
+// tile j is being scored, tile j-1 is being summed, tiles j+1 and j+2 are streaming in.
 //
 // Scores ([ase] Fig. 2: content dot plus position dot over the concatenated row) are computed
 // transposed, S^T = tile . q_hat^T, with v_mfma_f32_32x32x16_bf16: tokens on M, heads on N, so
 // every lane holds the 16 scores of one head and the softmax max/sum stay inside the lane plus
 // one v_permlane32_swap between the two lane halves.  The weighted latent sum ([ase] Fig. 4,
 // z = a.C, rotary columns never summed) is accumulated transposed as well, O^T += C^T . P^T,
-// with the 512 latent columns on M (16 blocks of 32) and heads on N: the per-head rescale of
-// the accumulator is again a per-lane scalar.  C^T operands come from ds_read_b64_tr_b16, the
-// gfx950 transposing LDS read, so the row-major tile needs no reshuffle.  The token order inside
-// each 16-wide MFMA k-step follows the score layout; both operands use the same order.
+// with the 512 latent columns on M (16 blocks of 32) and heads on N.  C^T operands come from
+// ds_read_b64_tr_b16, the gfx950 transposing LDS read, so the row-major tile needs no reshuffle.
+// The token order inside each 16-wide MFMA k-step follows the score layout; both operands use
+// the same order.
 //
-// Software pipeline per wave: the 36 dependent score MFMAs of tile j are interleaved with the
-// 32 independent weighted-sum MFMAs of tile j-1 (whose probabilities are ready), which hides the
-// latency of the dependent chain; the nine tile transfers of tile j+2 are spread over the same
-// phase so that issuing them never stalls the wave; the softmax of tile j follows.
+// Per tile and wave, phase A runs the 36 dependent score MFMAs of tile j (operands read three
+// steps ahead) with the nine transfers of tile j+2 spread over it; phase B runs the 32
+// independent weighted-sum MFMAs of tile j-1 with the softmax of tile j woven between them, so
+// that the VALU work hides behind the matrix cores.
 //
 // LDS tile layout: a latent region (32 rows x 1,024 B) followed by a rotary region (32 rows x
 // 128 B).  gfx950 LDS has 64 banks (256 B per cycle).  Latent 16-byte chunks are XOR-swizzled
@@ -35,12 +38,12 @@
 // transfers in flight target other buffers and would otherwise wait for them before every LDS
 // read.  M0 carries the LDS destination; this kernel has no other M0 user.
 //
-// Softmax uses base-2 logits (q_hat carries sm_scale*log2 e) against a fixed reference per chunk:
-// the maximum of the chunk's first tile.  Probabilities of later tiles may then exceed one, by
+// Softmax uses base-2 logits (q_hat carries sm_scale*log2 e) against a fixed reference per
+// segment: the maximum of its first tile.  Probabilities of later tiles may then exceed one, by
 // at most 2^64 (fp32 and bf16 keep their relative precision there), so the 256-register
 // accumulator is never rescaled inside the loop.  If some head's scores climb more than 64
-// above its reference, the workgroup runs the chunk a second time with the chunk maximum (now
-// known) as reference; with realistic scores that pass never happens.
+// above its reference, the workgroup runs the segment a second time with the segment maximum
+// (now known) as reference; with realistic scores that pass never happens.
 
 #include <math.h>
 

@@ -36,7 +36,7 @@ def compute_units(device=None) -> int:
     return int(torch.cuda.get_device_properties(torch.device(device or "cuda:0")).multi_processor_count)
 
 
-def balanced_units(lens, n_cu: int, min_tiles: int = 16) -> int:
+def balanced_units(lens, n_cu: int, min_tiles: int = 4) -> int:
     """Units of the balanced split for a batch: one per compute unit, fewer when that would leave
     a unit less than `min_tiles` tiles (MLA_BALANCED_TILE tokens each) of cache to read."""
     lens = np.asarray(lens, dtype=np.int64)
