@@ -375,52 +375,61 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         const unsigned char* gnext = tile_src(dma_next ? j + 2 : j);  // never look past the segment
         const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
 
-        // ---- phase A: scores of tile j, one dependent MFMA chain, operands read three steps
-        // ahead; the nine transfers of tile j+2 are spread over it
+        // ---- phase A: scores of tile j, one dependent MFMA chain, operands read kQA steps
+        // ahead; the nine transfers of tile j+2 are spread over it, and the first kPB operand
+        // reads of phase B are issued during its last steps
+        constexpr int kQA = 3, kPB = 3;
         f32x16 sacc;
 #pragma unroll
         for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
+        bf16x8 pa[kPB + 1];
         {
-          bf16x8 qa[4], qb[4];  // qb: rotary q_hat steps
+          bf16x8 qa[kQA + 1], qb[kQA + 1];  // qb: rotary q_hat steps
           auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
 #pragma unroll
-          for (int i = 0; i < 3; ++i) qa[i] = lds16(a_src(tb, i));
+          for (int i = 0; i < kQA; ++i) qa[i] = lds16(a_src(tb, i));
 #pragma unroll
           for (int i = 0; i < kKSteps; ++i) {
-            if (i + 3 < kKSteps) {
-              qa[(i + 3) % 4] = lds16(a_src(tb, i + 3));
-              if (i + 3 >= kKLat) qb[(i + 3) % 4] = lds16(b_src(i + 3));
+            if (i + kQA < kKSteps) {
+              qa[(i + kQA) % (kQA + 1)] = lds16(a_src(tb, i + kQA));
+              if (i + kQA >= kKLat) qb[(i + kQA) % (kQA + 1)] = lds16(b_src(i + kQA));
+            } else if (i + kQA - kKSteps < kPB) {
+              const int k = i + kQA - kKSteps;
+              pa[k] = tr8(tp, k);
             }
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % 4], i < kKLat ? qf[i] : qb[i % 4], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % (kQA + 1)], i < kKLat ? qf[i] : qb[i % (kQA + 1)],
+                                                           sacc, 0, 0, 0);
             if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
 
+        // tail tile: scores of tokens past the segment end drop out of the softmax
+        if (nvalid < kTile) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
+            if (tok >= nvalid) sacc[x] = -INFINITY;
+          }
+        }
+
         // ---- phase B: weighted sum of tile j-1 (32 independent MFMAs) with the online softmax of
         // tile j (base-2 logits; lane = one head, lanes l and l^32 share it) woven between them,
-        // so the VALU work runs in the shadow of the matrix cores.  Branch-free: the tail mask
-        // and the reference update are selects.
+        // so the VALU work runs in the shadow of the matrix cores.  Branch-free: the reference
+        // update is a select.
         {
-          bf16x8 pa[4];
-#pragma unroll
-          for (int i = 0; i < 3; ++i) pa[i] = tr8(tp, i);
           const bool first = pass == 0 && j == 0;  // the segment's first tile fixes the reference
           float mx0 = 0.f, mx = 0.f, pr[16];
           bf16x8 pn0, pn1;
 #pragma unroll
           for (int i = 0; i < kPvSteps; ++i) {
-            if (i + 3 < kPvSteps) pa[(i + 3) % 4] = tr8(tp, i + 3);
-            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 4], (i < kMBlk) ? pb0 : pb1, acc[i & 15],
-                                                                  0, 0, 0);
-            if (i == 1 || i == 2) {  // tail mask and row maximum, one half per step
+            if (i + kPB < kPvSteps) pa[(i + kPB) % (kPB + 1)] = tr8(tp, i + kPB);
+            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % (kPB + 1)], (i < kMBlk) ? pb0 : pb1,
+                                                                  acc[i & 15], 0, 0, 0);
+            if (i == 1 || i == 2) {  // row maximum, one half per step
               float m = -INFINITY;
 #pragma unroll
-              for (int x = 8 * (i - 1); x < 8 * i; ++x) {
-                const int tok = 8 * (x >> 2) + 4 * hi + (x & 3);
-                sacc[x] = tok < nvalid ? sacc[x] : -INFINITY;
-                m = fmaxf(m, sacc[x]);
-              }
+              for (int x = 8 * (i - 1); x < 8 * i; ++x) m = fmaxf(m, sacc[x]);
               if (i == 1) {
                 mx0 = m;
               } else {
@@ -477,17 +486,36 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       __syncthreads();
     }
 
-    // ---- normalise and write the segment's partial
+    // ---- normalise and write the segment's partial.  The MFMA layout gives each lane 16-byte
+    // pieces of 32 different rows; staged through LDS (the tile buffers are idle now), every store
+    // instruction writes 1 KiB of one contiguous row instead.
     const float l_tot = lane_swap_sum(l_lane);
     const float inv = 1.f / l_tot;
-    float* op = o_part + orow * kDc + 4 * hi;
+    __syncthreads();  // every wave is done with the tile buffers and the rerun flags
+    {
+      constexpr int kStRow = 256 * 4 + 16;  // one staged half row, padded against bank conflicts
+      lds_u8* const stg = lbase + wave * 32 * kStRow;
+      float* const orow0 = o_part + (slot * kH + wave * 32) * kDc;
 #pragma unroll
-    for (int mb = 0; mb < kMBlk; ++mb) {
-      const f32x16 v = acc[mb] * inv;
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4)
-        *reinterpret_cast<float4*>(op + 32 * mb + 8 * j4) = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int m = 0; m < 8; ++m) {
+          const f32x16 v = acc[8 * half + m] * inv;
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const u32x4 f = {__float_as_uint(v[4 * j4]), __float_as_uint(v[4 * j4 + 1]), __float_as_uint(v[4 * j4 + 2]),
+                             __float_as_uint(v[4 * j4 + 3])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+                stg + (lane & 31) * kStRow + 4 * (32 * m + 8 * j4 + 4 * hi)) = f;
+          }
+        }
+        // the same wave reads back what it wrote: LDS operations of one wave complete in order
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) {
+          const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stg + r * kStRow + 16 * lane);
+          *reinterpret_cast<u32x4*>(orow0 + size_t(r) * kDc + 256 * half + 4 * lane) = x;
+        }
+      }
     }
     if (hi == 0 && lse_part) lse_part[orow] = (m_ref + log2f(l_tot)) * kLn2;
     if constexpr (!kBal) break;
