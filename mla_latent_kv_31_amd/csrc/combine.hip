@@ -2,8 +2,8 @@
 //   LSE = ln sum_i exp(lse_i),  z = sum_i exp(lse_i - LSE) o_i
 // over any split equal to the single-pass softmax of the scores ([ase] Fig. 2).  One wave per
 // (sequence, head): lanes first reduce the chunk maxima and weights (kept in LDS), then each lane
-// accumulates eight latent columns over the chunks with 16-byte loads; chunks of weight zero
-// (empty or negligible) are never read.  The balanced split (schedule.h) merges the slots of each
+// accumulates eight latent columns over the chunks with 16-byte loads, eight chunks' loads in
+// flight at a time; chunks of weight zero (empty or negligible) never contribute.  The balanced split (schedule.h) merges the slots of each
 // sequence's segments.
 
 #include <math.h>
@@ -68,13 +68,31 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
   if (c0 < dc) {
     const float* op = o_part + (size_t(base) * H + h) * dc + c0;
     const size_t stride = size_t(H) * dc;
-    for (int s = 0; s < count; ++s) {
-      const float w = wts[wave][s] * inv;
-      if (w == 0.f) continue;  // empty chunk (its partial may be unwritten) or negligible weight
-      const float4 x0 = *reinterpret_cast<const float4*>(op + s * stride);
-      const float4 x1 = *reinterpret_cast<const float4*>(op + s * stride + 4);
-      a0.x = fmaf(w, x0.x, a0.x); a0.y = fmaf(w, x0.y, a0.y); a0.z = fmaf(w, x0.z, a0.z); a0.w = fmaf(w, x0.w, a0.w);
-      a1.x = fmaf(w, x1.x, a1.x); a1.y = fmaf(w, x1.y, a1.y); a1.z = fmaf(w, x1.z, a1.z); a1.w = fmaf(w, x1.w, a1.w);
+    // eight slots per round: all sixteen loads are issued before the first FMA.  Rows of zero
+    // weight (empty chunks, possibly never written) are loaded but dropped by a select.
+    constexpr int kG = 8;
+    for (int s0 = 0; s0 < count; s0 += kG) {
+      float4 x0[kG], x1[kG];
+      float w[kG];
+#pragma unroll
+      for (int k = 0; k < kG; ++k) {
+        const int s = min(s0 + k, count - 1);
+        w[k] = s0 + k < count ? wts[wave][s] * inv : 0.f;
+        x0[k] = *reinterpret_cast<const float4*>(op + s * stride);
+        x1[k] = *reinterpret_cast<const float4*>(op + s * stride + 4);
+      }
+#pragma unroll
+      for (int k = 0; k < kG; ++k) {
+        const bool use = w[k] != 0.f;
+        a0.x = use ? fmaf(w[k], x0[k].x, a0.x) : a0.x;
+        a0.y = use ? fmaf(w[k], x0[k].y, a0.y) : a0.y;
+        a0.z = use ? fmaf(w[k], x0[k].z, a0.z) : a0.z;
+        a0.w = use ? fmaf(w[k], x0[k].w, a0.w) : a0.w;
+        a1.x = use ? fmaf(w[k], x1[k].x, a1.x) : a1.x;
+        a1.y = use ? fmaf(w[k], x1[k].y, a1.y) : a1.y;
+        a1.z = use ? fmaf(w[k], x1[k].z, a1.z) : a1.z;
+        a1.w = use ? fmaf(w[k], x1[k].w, a1.w) : a1.w;
+      }
     }
     *reinterpret_cast<float4*>(zo + c0) = a0;
     *reinterpret_cast<float4*>(zo + c0 + 4) = a1;

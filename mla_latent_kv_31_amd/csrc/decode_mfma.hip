@@ -21,7 +21,7 @@
 // the same order.
 //
 // Per tile and wave, phase A runs the 36 dependent score MFMAs of tile j (operands read three
-// steps ahead) with the nine transfers of tile j+2 spread over it; phase B runs the 32
+// steps ahead) with the nine transfers of tile j+2 issued in its first steps; phase B runs the 32
 // independent weighted-sum MFMAs of tile j-1 with the softmax of tile j woven between them, so
 // that the VALU work hides behind the matrix cores.
 //
@@ -376,7 +376,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
 
         // ---- phase A: scores of tile j, one dependent MFMA chain, operands read kQA steps
-        // ahead; the nine transfers of tile j+2 are spread over it, and the first kPB operand
+        // ahead; the nine transfers of tile j+2 go out in its first steps, and the first kPB operand
         // reads of phase B are issued during its last steps
         constexpr int kQA = 3, kPB = 3;
         f32x16 sacc;
@@ -399,7 +399,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
             }
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % (kQA + 1)], i < kKLat ? qf[i] : qb[i % (kQA + 1)],
                                                            sacc, 0, 0, 0);
-            if ((i & 3) == 1) dma_one(dma_next, gnext, dnext, i >> 2);
+            if (i >= 1 && i <= kDmaPerWave) dma_one(dma_next, gnext, dnext, i - 1);  // early: more lead time
             __builtin_amdgcn_sched_barrier(0);
           }
         }

@@ -86,16 +86,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) bq[rb][ks] = r < R ? load_bf16x8(qrow + 16 * ks) : bf16x8{};
   }
+  // A operands of all four column blocks, loaded together with the B operands so that the wave
+  // waits for memory once
   const uint16_t* wbase = w_uk + (size_t(h) * kDc + 128 * wave + (lane & 31)) * kDk + 8 * hi;
-  bf16x8 a[2][kDk / 16];  // A operands of the current and the next column block
+  bf16x8 a[4][kDk / 16];
 #pragma unroll
-  for (int ks = 0; ks < kDk / 16; ++ks) a[0][ks] = load_bf16x8(wbase + 16 * ks);
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int ks = 0; ks < kDk / 16; ++ks) a[jb][ks] = load_bf16x8(wbase + size_t(32 * jb) * kDk + 16 * ks);
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
-    if (jb + 1 < 4) {
-#pragma unroll
-      for (int ks = 0; ks < kDk / 16; ++ks) a[(jb + 1) & 1][ks] = load_bf16x8(wbase + size_t(32 * (jb + 1)) * kDk + 16 * ks);
-    }
     f32x16 acc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
     for (int ks = 0; ks < kDk / 16; ++ks)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jb & 1][ks], bq[rb][ks], acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jb][ks], bq[rb][ks], acc[rb], 0, 0, 0);
     // D layout: lane holds row 32rb + lane%32 and columns j = 128w + 32jb + 8g + 4hi + 0..3
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -191,7 +191,7 @@ __device__ __forceinline__ void out_proj_rows(const lds_u8* lw, int H, int R, in
   f32x16 acc0, acc1;
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc0[x] = acc1[x] = 0.f;
-  constexpr int kPre = 2;  // z steps loaded ahead
+  constexpr int kPre = TWO ? 4 : 8;  // z steps loaded ahead: enough bytes in flight to cover HBM latency
   float4 ra0[kPre], ra1[kPre], rb0[kPre], rb1[kPre];
 #pragma unroll
   for (int p = 0; p < kPre; ++p) {
@@ -254,11 +254,19 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(int H, int R, const 
   if (!xcd_head_map(kHalves * slices, H, h, inner)) return;
   const int v0 = kOpCols * (inner % kHalves), rs = inner / kHalves;
   const int wave = threadIdx.x >> 6;
-  // stage W_UV[h][:, v0 .. v0+63]: 512 rows x 8 chunks of 16 B
-  for (int c = threadIdx.x; c < kDc * 8; c += blockDim.x) {
-    const int j = c >> 3, ch = c & 7;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(w_uv + (size_t(h) * kDc + j) * kDv + v0 + 8 * ch);
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lw + j * kOpRowB + 16 * op_chunk(j, ch)) = v;
+  // stage W_UV[h][:, v0 .. v0+63]: 512 rows x 8 chunks of 16 B, 16 per thread, all loads issued
+  // before the first LDS write
+  constexpr int kPer = kDc * 8 / 256;
+  u32x4 wv[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = threadIdx.x + 256 * k, j = c >> 3, ch = c & 7;
+    wv[k] = *reinterpret_cast<const u32x4*>(w_uv + (size_t(h) * kDc + j) * kDv + v0 + 8 * ch);
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = threadIdx.x + 256 * k, j = c >> 3, ch = c & 7;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lw + j * kOpRowB + 16 * op_chunk(j, ch)) = wv[k];
   }
   __syncthreads();
   const int rbA = kOpRows * rs + 32 * (wave >> 1);
