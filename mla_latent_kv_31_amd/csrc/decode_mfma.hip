@@ -155,8 +155,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
   // transfer; rotary rows 8*wave .. 8*wave+7 are this wave's ninth.  Lane L writes LDS chunk L of
   // the transfer; the global chunk it reads is the one that the XOR swizzle places there.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // (lane & ~15) | ((lane ^ c) & 15) = lane ^ c for a 4-bit c: one XOR with a scalar per transfer
+  // from a single per-lane base (kept opaque in the tile loop, so no per-transfer copies are held)
+  uint32_t lane16 = 16u * uint32_t(lane);
   auto lat_off = [&](int x) {  // the swizzle of row n = 4x + wave depends on n & 15
-    return uint32_t(16 * ((lane & ~15) | ((lane ^ lat_swz(4 * (x & 3) + wave_u)) & 15)));
+    return lane16 ^ uint32_t(16 * lat_swz(4 * (x & 3) + wave_u));
   };
   auto rope_off = [&]() {
     return uint32_t((lane >> 3) * kRowB + kLatB + 16 * ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)));
@@ -353,7 +356,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         __syncthreads();  // every wave's part of tile j landed; tile j-2 fully consumed
         // Keep the per-step offsets derived inside the loop (one XOR each) instead of letting the
         // compiler hoist a dozen precomputed copies into registers next to the q_hat fragments.
-        asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(qq_x), "+v"(pv_x), "+v"(pv_d8));
+        asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(qq_x), "+v"(pv_x), "+v"(pv_d8), "+v"(lane16));
         lds_u8* const tb = lbase + (j % kNBuf) * kTileB;
         lds_u8* const tp = lbase + ((j + kNBuf - 1) % kNBuf) * kTileB;
         const int nvalid = min(kTile, t1 - (t0 + j * kTile));
