@@ -5,10 +5,17 @@
 //
 // A workgroup runs a list of segments (query row, sequence, token range, output row): one chunk
 // of the fixed split, all segments of one unit of the work-balanced split (schedule.h), or one
-// prefill row.  Four waves; wave w owns heads 32w..32w+31 for the whole segment.  All 128 heads
-// read the same cached rows, so each 32-token tile (36,864 B) is fetched from HBM once per
-// workgroup, straight into LDS with 16-byte global_load_lds transfers.  Four LDS buffers rotate:
-// tile j is being scored, tile j-1 is being summed, tiles j+1 and j+2 are streaming in.
+// prefill row.  Four waves.  All 128 heads read the same cached rows, so each 32-token tile
+// (36,864 B) is fetched from HBM once per workgroup, straight into LDS with 16-byte
+// global_load_lds transfers.  Four LDS buffers rotate: tile j is being scored, tile j-1 is being
+// summed, tiles j+1 and j+2 are streaming in.
+//
+// Wave w scores heads 32w..32w+31 and runs their softmax.  The weighted sum is split the other
+// way: waves 2p and 2p+1 (a pair) both accumulate heads 64p..64p+63, wave 2p latent columns
+// 0..255 and wave 2p+1 columns 256..511.  Each wave hands its bf16 probabilities of a tile to
+// its partner through LDS, so every transposing operand read feeds two MFMAs (one per head
+// block of the pair) and the weighted sum needs half the LDS reads of a one-wave-per-head-block
+// split, with the same 256-register accumulator.
 //
 // Scores ([ase] Fig. 2: content dot plus position dot over the concatenated row) are computed
 // transposed, S^T = tile . q_hat^T, with v_mfma_f32_32x32x16_bf16: tokens on M, heads on N, so
@@ -21,9 +28,10 @@
 // the same order.
 //
 // Per tile and wave, phase A runs the 36 dependent score MFMAs of tile j (operands read three
-// steps ahead) with the nine transfers of tile j+2 issued in its first steps; phase B runs the 32
-// independent weighted-sum MFMAs of tile j-1 with the softmax of tile j woven between them, so
-// that the VALU work hides behind the matrix cores.
+// steps ahead) with the nine transfers of tile j+2 issued in its first steps, and picks up the
+// partner's probabilities of tile j-1; phase B runs the 32 independent weighted-sum MFMAs of tile
+// j-1 with the softmax of tile j woven between them, so that the VALU work hides behind the
+// matrix cores, and publishes this wave's probabilities of tile j for the partner.
 //
 // LDS tile layout: a latent region (32 rows x 1,024 B) followed by a rotary region (32 rows x
 // 128 B).  gfx950 LDS has 64 banks (256 B per cycle).  Latent 16-byte chunks are XOR-swizzled
@@ -74,9 +82,14 @@ constexpr int kLatPerWave = kTile / kWaves;      // 8 latent-row transfers per w
 constexpr int kDmaPerWave = kLatPerWave + 1;     // + 1 rotary transfer (8 rotary rows)
 constexpr int kKSteps = kW / 16;                 // 36 score k-steps
 constexpr int kKLat = kDc / 16;                  // 32 of them over the latent columns
-constexpr int kQrOff = kNBuf * kTileB;           // q_hat rotary parts of all heads: 128 x 128 B
-constexpr int kMBlk = kDc / 32;                  // 16 accumulator blocks
-constexpr int kPvSteps = 2 * kMBlk;              // 32 weighted-sum MFMAs per tile
+constexpr int kXWaveB = 2 * 64 * 16;             // one wave's bf16 probabilities of a tile (2 k-steps)
+constexpr int kXBufB = kWaves * kXWaveB;         // probability exchange of one tile: 8 KiB
+constexpr int kXOff = kNBuf * kTileB;            // two exchange buffers (tiles of even / odd index)
+constexpr int kLdsB = kXOff + 2 * kXBufB;        // 160 KiB: the whole CU
+constexpr int kMBlk = kDc / 2 / 32;              // 8 latent blocks of 32 columns per wave
+constexpr int kAcc = 2 * kMBlk;                  // x 2 head blocks = 16 accumulator blocks
+constexpr int kPvOps = 2 * kMBlk;                // 16 transposed operands per tile (2 k-steps)
+constexpr int kPvSteps = 2 * kPvOps;             // 32 weighted-sum MFMAs per tile
 constexpr float kRerunMargin = 64.0f;  // reference may lag the running max by this much
 
 __host__ __device__ constexpr int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
@@ -93,11 +106,18 @@ __device__ __forceinline__ float lane_swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float* p) {
-  bf16x8 r;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) r[x] = (__bf16)p[x];
-  return r;
+// One step of the score chain, accumulated in VGPRs (the 256 accumulator registers hold the
+// weighted sums).  The first step starts from zero; consecutive steps accumulate into exactly the
+// same registers, which the matrix core forwards; after the last one the wave waits out the
+// result latency before any VALU instruction reads the scores.
+__device__ __forceinline__ void score_step(bool first, bool last, f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if (first) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  } else if (last) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(acc) : "v"(a), "v"(b));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  }
 }
 
 __device__ __forceinline__ bf16x8 lds16(const lds_u8* p) {
@@ -107,13 +127,6 @@ __device__ __forceinline__ bf16x8 lds16(const lds_u8* p) {
 __device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const unsigned char* gbase) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase)
                : "memory");
-}
-// The same transfer, skipped when `go` is zero (wave-uniform).  The branch lives inside the asm so
-// the unrolled MFMA phase it sits in stays one basic block for the register allocator.
-__device__ __forceinline__ void dma16_if(uint32_t go, uint32_t lds_dst, uint32_t voff, const unsigned char* gbase) {
-  asm volatile("s_cmp_eq_u32 %0, 0\n\ts_cbranch_scc1 .Lmla_skip%=\n\ts_mov_b32 m0, %1\n\t"
-               "global_load_lds_dwordx4 %2, %3\n.Lmla_skip%=:" ::"s"(go), "s"(lds_dst), "v"(voff), "s"(gbase)
-               : "memory", "scc");
 }
 
 // Page ids of 64 consecutive pages of a sequence's table, one per lane, loaded and waited for in
@@ -143,12 +156,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
                         int split_tokens, const int32_t* __restrict__ q_start, float* __restrict__ o_part,
                         float* __restrict__ lse_part) {
   constexpr bool kBal = MODE == kBalanced;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kNBuf * kTileB + kH * kRopeB];  // 160 KiB
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsB];
   lds_u8* const lbase = (lds_u8*)smem;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hi = lane >> 5;
-  const int head = wave * 32 + (lane & 31);
+  const int head = wave * 32 + (lane & 31);  // scored by this lane (lanes l and l^32 share it)
+  const int lh = wave & 1;                   // latent half summed by this wave
   const int cap = max_pages * page_size;  // never index past the page table
 
   // ---- per-lane constants of the tile transfers.  Latent row n = 4x + wave (x < 8) is one 1 KiB
@@ -170,32 +184,36 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
   // score reads: row (lane&31), logical chunk 2k + hi (latent) or 2(k-32) + hi (rotary).  The
   // swizzle XORs the chunk index, so the place of step k is the place of step 0 XOR 32*k bytes
   // (k < 8 within a 256-byte block; rotary k < 4).
-  int qk_x, qr_x, qq_x;
+  int qk_x, qr_x;
   {
     const int fl = lat_swz(lane & 15), gr = rope_swz(lane & 31);
     qk_x = (lane & 31) * kLatB + 16 * (hi ^ fl);
     qr_x = kRopeOff + (lane & 31) * kRopeB + 16 * (hi ^ gr);
-    qq_x = kQrOff + head * kRopeB + 16 * (hi ^ rope_swz(head));  // head & 15 == lane & 15
   }
   // transposing reads: lane group g = lane/16 reads rows r0 = 4*(g/2) + (lane%16)/4 (+16a, +8 for
-  // the second half of the k-step), columns 32*mb + 16*(g%2) + 4*(lane%4) .. +3.  Column block
-  // 4*m4 + y lands at the place of m4 = 0 XOR 64*m4; the row +8 flips bit 1 of the swizzle, so
-  // the second read sits a fixed per-lane distance from the first.
+  // the second half of the k-step), columns 32*mb + 16*(g%2) + 4*(lane%4) .. +3 of this wave's
+  // latent half.  Column block 4*m4 + y lands at the place of m4 = 0 XOR 64*m4; the row +8 flips
+  // bit 1 of the swizzle, so the second read sits a fixed per-lane distance from the first.
   int pv_x, pv_d8;
   {
     const int g = lane >> 4, ii = lane & 15, qq = ii & 3;
     const int r0 = 4 * (g >> 1) + (ii >> 2);
     const int y = 2 * (g & 1) + (qq >> 1);
-    pv_x = r0 * kLatB + 16 * (y ^ lat_swz(r0)) + 8 * (qq & 1);
+    pv_x = r0 * kLatB + 512 * lh + 16 * (y ^ lat_swz(r0)) + 8 * (qq & 1);
     pv_d8 = 8 * kLatB + 16 * (((4 + y) ^ lat_swz(8 + r0)) - ((4 + y) ^ lat_swz(r0)));
   }
+  // probability exchange: this lane's 16 bytes of k-step s in the buffer of tile parity t
+  const uint32_t x_mine = uint32_t(kXOff + wave * kXWaveB + 16 * lane);
+  const uint32_t x_peer = uint32_t(kXOff + (wave ^ 1) * kXWaveB + 16 * lane);
+  auto x_at = [&](uint32_t base, int t, int s) { return lbase + base + t * kXBufB + s * 1024; };
   auto a_src = [&](const lds_u8* tb, int kk) -> const lds_u8* {
     return kk < kDc / 16 ? tb + 256 * (kk >> 3) + (qk_x ^ (32 * (kk & 7))) : tb + (qr_x ^ (32 * (kk & 3)));
   };
-  // weighted-sum operand i = 16 * kstep + mb: two transposing reads, tokens +0..3 / +8..11
-  auto tr8 = [&](const lds_u8* tb, int i) {
-    const lds_u8* base = tb + 16 * (i >> 4) * kLatB + 256 * ((i & 15) >> 2);
-    const lds_u8* p0 = base + (pv_x ^ (64 * (i & 3)));
+  // weighted-sum operand o = 8 * kstep + mb (mb: block of this wave's latent half): two
+  // transposing reads, tokens +0..3 / +8..11
+  auto tr8 = [&](const lds_u8* tb, int o) {
+    const lds_u8* base = tb + 16 * (o >> 3) * kLatB + 256 * ((o & 7) >> 2);
+    const lds_u8* p0 = base + (pv_x ^ (64 * (o & 3)));
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
     const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + pv_d8));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -275,38 +293,32 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       const int in_page = (kt & ((1 << tiles_per_page_log2) - 1)) * kTile;
       return reinterpret_cast<const unsigned char*>(pool + (size_t(pg) * page_size + in_page) * kW);
     };
-    auto dma_one = [&](uint32_t go, const unsigned char* g, uint32_t dst, int x) {  // x-th transfer
+    auto dma_one = [&](const unsigned char* g, uint32_t dst, int x) {  // x-th transfer of a tile
       if (x < kLatPerWave) {
         const int n = 4 * x + wave_u;
-        dma16_if(go, dst + uint32_t(n * kLatB), lat_off(x), g + size_t(n) * kRowB);
+        dma16(dst + uint32_t(n * kLatB), lat_off(x), g + size_t(n) * kRowB);
       } else {
-        dma16_if(go, dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), g + size_t(8 * wave_u) * kRowB);
+        dma16(dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), g + size_t(8 * wave_u) * kRowB);
       }
     };
     auto dma_tile = [&](int k) {
       const unsigned char* g = tile_src(k);
       const uint32_t dst = lds0 + uint32_t((k % kNBuf) * kTileB);
 #pragma unroll
-      for (int x = 0; x < kDmaPerWave; ++x) dma_one(1u, g, dst, x);
+      for (int x = 0; x < kDmaPerWave; ++x) dma_one(g, dst, x);
     };
 
     dma_tile(0);
 
-    // ---- this wave's 32 heads of q_hat, as the B operand of S^T = tile . q_hat^T: the 512 latent
-    // columns stay in registers; the 64 rotary columns of all heads go to LDS (swizzled like the
-    // tile's rotary rows), which keeps the register file within budget.
-    bf16x8 qf[kKLat];
+    // ---- this wave's 32 heads of q_hat, as the B operand of S^T = tile . q_hat^T, held in
+    // registers for the whole segment: 32 latent and 4 rotary k-steps.
+    bf16x8 qf[kKLat], rq[kKSteps - kKLat];
     {
       const uint16_t* qp = q_hat + (qrow * kH + head) * kW + 8 * hi;
 #pragma unroll
       for (int k = 0; k < kKLat; ++k) qf[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
-      const uint16_t* qb = q_hat + qrow * kH * kW + kDc;
 #pragma unroll
-      for (int x = 0; x < kH * kRopeB / 16 / kThreads; ++x) {  // 4 chunks of 16 B per thread
-        const int c = threadIdx.x + x * kThreads, h = c >> 3, ch = c & 7;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + size_t(h) * kW + 8 * ch);
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + kQrOff + h * kRopeB + 16 * (ch ^ rope_swz(h))) = v;
-      }
+      for (int k = 0; k < kKSteps - kKLat; ++k) rq[k] = *reinterpret_cast<const bf16x8*>(qp + kDc + 16 * k);
     }
     // Consume these loads here: an empty asm that reads every fragment makes the compiler wait for
     // them before the tile loop (tile 0 and the previous segment's stores complete too).  Otherwise
@@ -314,11 +326,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     // transfers in flight.
 #pragma unroll
     for (int k = 0; k < kKLat; ++k) asm volatile("" : "+v"(qf[k]));
+#pragma unroll
+    for (int k = 0; k < kKSteps - kKLat; ++k) asm volatile("" : "+v"(rq[k]));
     if (ntiles > 1) dma_tile(1);
 
-    f32x16 acc[kMBlk];
+    f32x16 acc[kAcc];  // acc[2 * mb + 0]: own heads, acc[2 * mb + 1]: the partner's
     float m_ref = -INFINITY, m_max = -INFINITY, l_lane = 0.f;
-    bf16x8 pb0, pb1;  // probabilities of the previous tile, bf16, k-steps 0 and 1
+    bf16x8 pb0, pb1;  // own probabilities of the previous tile, bf16, k-steps 0 and 1
 
     for (int pass = 0; pass < 2; ++pass) {
       if (pass > 0) {
@@ -329,10 +343,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         dma_tile(0);
         if (ntiles > 1) dma_tile(1);
       }
+      // source of the transfers issued in the next tile step: tile j+2 of step j, or, past the
+      // segment end, a harmless copy of its last tile into the buffer that is free anyway
+      const unsigned char* g_dma = tile_src(min(2, ntiles - 1));
 #pragma unroll
-      for (int mb = 0; mb < kMBlk; ++mb)
+      for (int a = 0; a < kAcc; ++a)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[mb][x] = 0.f;
+        for (int x = 0; x < 16; ++x) acc[a][x] = 0.f;
       l_lane = 0.f;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
@@ -340,15 +357,25 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         pb1[x] = (__bf16)0.f;
       }
       // The weighted sum of the tile before tile 0 runs on a zeroed buffer with zero
-      // probabilities, which keeps the pipelined loop uniform.
+      // probabilities (own and, in the exchange buffer of odd tiles, the partner's), which keeps
+      // the pipelined loop uniform.
       {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         for (int x = threadIdx.x; x < kRopeOff / 16; x += kThreads)
           *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + (kNBuf - 1) * kTileB + 16 * x) = zero;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(x_at(x_mine, 1, 0)) = zero;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(x_at(x_mine, 1, 1)) = zero;
       }
 
       bool over = false;
       for (int j = 0; j < ntiles; ++j) {
+        // A segment longer than 64 pages moves its page window once tile j+3, whose address this
+        // step computes, leaves it (the wait inside the load also drains tile j+1, a bubble every
+        // 64 pages).  Tiles whose addresses are already computed are not affected.
+        if (j + 3 < ntiles && ((kt0 + j + 3) >> tiles_per_page_log2) - p0 - wbase >= 64) {
+          wbase += 64;
+          my_page = load_page_window(pt_row, p0 + wbase, npg - wbase, max_pages, lane);
+        }
         if (j + 1 < ntiles)
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");  // tile j landed, j+1 may fly
         else
@@ -356,7 +383,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         __syncthreads();  // every wave's part of tile j landed; tile j-2 fully consumed
         // Keep the per-step offsets derived inside the loop (one XOR each) instead of letting the
         // compiler hoist a dozen precomputed copies into registers next to the q_hat fragments.
-        asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(qq_x), "+v"(pv_x), "+v"(pv_d8), "+v"(lane16));
+        asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(pv_x), "+v"(pv_d8), "+v"(lane16));
         lds_u8* const tb = lbase + (j % kNBuf) * kTileB;
         lds_u8* const tp = lbase + ((j + kNBuf - 1) % kNBuf) * kTileB;
         const int nvalid = min(kTile, t1 - (t0 + j * kTile));
@@ -366,43 +393,37 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
             *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tb + nvalid * kLatB + 16 * x) = zero;
           __syncthreads();
         }
-        // tiles left after tile j+1: nonzero when tile j+2 is to be fetched.  A count, not a
-        // flag: a boolean would be narrowed to a lane mask and leave the scalar operand it feeds.
-        const uint32_t dma_next = __builtin_amdgcn_readfirstlane(uint32_t(max(ntiles - j - 2, 0)));
-        // A segment longer than 64 pages moves its page window once tile j+2 leaves it (the wait
-        // inside the load also drains tile j+1, a bubble every 64 pages).
-        if (dma_next && ((kt0 + j + 2) >> tiles_per_page_log2) - p0 - wbase >= 64) {
-          wbase += 64;
-          my_page = load_page_window(pt_row, p0 + wbase, npg - wbase, max_pages, lane);
-        }
-        const unsigned char* gnext = tile_src(dma_next ? j + 2 : j);  // never look past the segment
+        // Tile j+2 goes to the buffer that tile j-2 left; past the segment end the transfers copy
+        // the segment's last tile there instead, which keeps the wait counts uniform and the loop
+        // free of branches.  Every transfer lands before the loop ends (drained below).
         const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
+        const unsigned char* g_dma_next = g_dma;
 
         // ---- phase A: scores of tile j, one dependent MFMA chain, operands read kQA steps
-        // ahead; the nine transfers of tile j+2 go out in its first steps, and the first kPB operand
-        // reads of phase B are issued during its last steps
+        // ahead; the nine transfers of tile j+2 go out in its first steps, the partner's
+        // probabilities of tile j-1 are read after them, and the first kPB operand reads of phase B
+        // are issued during its last steps
         constexpr int kQA = 3, kPB = 3;
         f32x16 sacc;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[x] = 0.f;
-        bf16x8 pa[kPB + 1];
+        bf16x8 pa[kPB + 1], pq0, pq1;
         {
-          bf16x8 qa[kQA + 1], qb[kQA + 1];  // qb: rotary q_hat steps
-          auto b_src = [&](int kk) -> const lds_u8* { return lbase + (qq_x ^ (32 * (kk & 3))); };
+          bf16x8 qa[kQA + 1];
 #pragma unroll
           for (int i = 0; i < kQA; ++i) qa[i] = lds16(a_src(tb, i));
+          __builtin_amdgcn_sched_barrier(0);  // the first operand reads go out right after the barrier
 #pragma unroll
           for (int i = 0; i < kKSteps; ++i) {
             if (i + kQA < kKSteps) {
               qa[(i + kQA) % (kQA + 1)] = lds16(a_src(tb, i + kQA));
-              if (i + kQA >= kKLat) qb[(i + kQA) % (kQA + 1)] = lds16(b_src(i + kQA));
             } else if (i + kQA - kKSteps < kPB) {
               const int k = i + kQA - kKSteps;
               pa[k] = tr8(tp, k);
             }
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[i % (kQA + 1)], i < kKLat ? qf[i] : qb[i % (kQA + 1)],
-                                                           sacc, 0, 0, 0);
-            if (i >= 1 && i <= kDmaPerWave) dma_one(dma_next, gnext, dnext, i - 1);  // early: more lead time
+            if (i == kDmaPerWave + 2) pq0 = lds16(x_at(x_peer, (j + 1) & 1, 0));
+            if (i == kDmaPerWave + 3) pq1 = lds16(x_at(x_peer, (j + 1) & 1, 1));
+            score_step(i == 0, i == kKSteps - 1, sacc, qa[i % (kQA + 1)], i < kKLat ? qf[i] : rq[i - kKLat]);
+            if (i % 4 == 1) dma_one(g_dma, dnext, i / 4);
+            if (i == 22) g_dma_next = tile_src(min(j + 3, ntiles - 1));  // for the next step
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -416,19 +437,21 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
           }
         }
 
-        // ---- phase B: weighted sum of tile j-1 (32 independent MFMAs) with the online softmax of
-        // tile j (base-2 logits; lane = one head, lanes l and l^32 share it) woven between them,
-        // so the VALU work runs in the shadow of the matrix cores.  Branch-free: the reference
-        // update is a select.
+        // ---- phase B: weighted sum of tile j-1 (16 operands x 2 head blocks = 32 independent
+        // MFMAs) with the online softmax of tile j (base-2 logits; lane = one head, lanes l and l^32
+        // share it) woven between them, so the VALU work runs in the shadow of the matrix cores.
+        // Branch-free: the reference update is a select.
         {
           const bool first = pass == 0 && j == 0;  // the segment's first tile fixes the reference
-          float mx0 = 0.f, mx = 0.f, pr[16];
+          float mx0 = 0.f, mx = 0.f, pr[16], tsum = 0.f;
           bf16x8 pn0, pn1;
 #pragma unroll
           for (int i = 0; i < kPvSteps; ++i) {
-            if (i + kPB < kPvSteps) pa[(i + kPB) % (kPB + 1)] = tr8(tp, i + kPB);
-            acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % (kPB + 1)], (i < kMBlk) ? pb0 : pb1,
-                                                                  acc[i & 15], 0, 0, 0);
+            const int o = i >> 1, nb = i & 1;  // operand, head block (0: own, 1: partner)
+            if (nb == 0 && o + kPB < kPvOps) pa[(o + kPB) % (kPB + 1)] = tr8(tp, o + kPB);
+            const bf16x8 pp = o < kMBlk ? (nb ? pq0 : pb0) : (nb ? pq1 : pb1);
+            acc[2 * (o & 7) + nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[o % (kPB + 1)], pp, acc[2 * (o & 7) + nb], 0, 0, 0);
             if (i == 1 || i == 2) {  // row maximum, one half per step
               float m = -INFINITY;
 #pragma unroll
@@ -441,37 +464,51 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
                 m_max = fmaxf(m_max, mx);
                 over |= mx > m_ref + kRerunMargin;
               }
-            } else if (i >= 3 && i < 11) {  // two probabilities per step
-              const int x = 2 * (i - 3);
-              pr[x] = fast_exp2(sacc[x] - m_ref);
-              pr[x + 1] = fast_exp2(sacc[x + 1] - m_ref);
-            } else if (i == 11) {
-              float t = 0.f;
-#pragma unroll
-              for (int x = 0; x < 16; ++x) t += pr[x];
-              l_lane += t;
-            } else if (i == 12) {
-              pn0 = pack8(&pr[0]);
-            } else if (i == 13) {
-              pn1 = pack8(&pr[8]);
             }
+            // one probability per step (the exp2 is a quarter-rate instruction), summed and
+            // packed to bf16 pairwise as they come, so that no step outgrows its MFMA
+            if (i >= 3 && i < 19) pr[i - 3] = fast_exp2(sacc[i - 3] - m_ref);
+            if (i == 4) tsum = pr[0];
+            if (i >= 5 && i < 20) tsum += pr[i - 4];
+            if (i >= 5 && i < 20 && (i & 1)) {  // pair (i-5)/2 is complete
+              const int x = i - 5;
+              if (x < 8) {
+                pn0[x] = (__bf16)pr[x];
+                pn0[x + 1] = (__bf16)pr[x + 1];
+              } else {
+                pn1[x - 8] = (__bf16)pr[x];
+                pn1[x - 7] = (__bf16)pr[x + 1];
+              }
+            }
+            if (i == 20) l_lane += tsum;
+            // for the partner, read after the next tile's barrier
+            if (i == 13) *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(x_at(x_mine, j & 1, 0)) = pn0;
+            if (i == 21) *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(x_at(x_mine, j & 1, 1)) = pn1;
             __builtin_amdgcn_sched_barrier(0);
           }
           pb0 = pn0;
           pb1 = pn1;
+          g_dma = g_dma_next;
         }
       }
 
-      // ---- weighted sum of the last tile
+      // ---- weighted sum of the last tile, once the partner's probabilities of it are published
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
       {
         lds_u8* const tp = lbase + ((ntiles - 1) % kNBuf) * kTileB;
+        const bf16x8 pq0 = lds16(x_at(x_peer, (ntiles - 1) & 1, 0));
+        const bf16x8 pq1 = lds16(x_at(x_peer, (ntiles - 1) & 1, 1));
         bf16x8 pa[3];
         pa[0] = tr8(tp, 0);
         pa[1] = tr8(tp, 1);
 #pragma unroll
         for (int i = 0; i < kPvSteps; ++i) {
-          if (i + 2 < kPvSteps) pa[(i + 2) % 3] = tr8(tp, i + 2);
-          acc[i & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i % 3], (i < kMBlk) ? pb0 : pb1, acc[i & 15], 0, 0, 0);
+          const int o = i >> 1, nb = i & 1;
+          if (nb == 0 && o + 2 < kPvOps) pa[(o + 2) % 3] = tr8(tp, o + 2);
+          const bf16x8 pp = o < kMBlk ? (nb ? pq0 : pb0) : (nb ? pq1 : pb1);
+          acc[2 * (o & 7) + nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[o % 3], pp, acc[2 * (o & 7) + nb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -489,21 +526,27 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       __syncthreads();
     }
 
-    // ---- normalise and write the segment's partial.  The MFMA layout gives each lane 16-byte
-    // pieces of 32 different rows; staged through LDS (the tile buffers are idle now), every store
-    // instruction writes 1 KiB of one contiguous row instead.
+    // ---- normalise and write the segment's partial.  The sums of the partner's heads come
+    // through the exchange buffer that no tile uses any more.  The MFMA layout gives each lane
+    // 16-byte pieces of 32 different rows; staged through LDS (the tile buffers are idle now),
+    // every store instruction writes 1 KiB of one contiguous half row instead.
     const float l_tot = lane_swap_sum(l_lane);
-    const float inv = 1.f / l_tot;
-    __syncthreads();  // every wave is done with the tile buffers and the rerun flags
+    __attribute__((address_space(3))) float* const l_x =
+        reinterpret_cast<__attribute__((address_space(3))) float*>(lbase + kXOff + (ntiles & 1) * kXBufB);
+    if (hi == 0) l_x[head] = l_tot;
+    __syncthreads();  // every wave is done with the tile buffers and the rerun flags; sums published
+    const float inv_own = 1.f / l_tot, inv_peer = 1.f / l_x[(wave ^ 1) * 32 + (lane & 31)];
     {
       constexpr int kStRow = 256 * 4 + 16;  // one staged half row, padded against bank conflicts
+      static_assert(kWaves * 32 * kStRow <= kXOff, "staging stays clear of the exchange buffers");
       lds_u8* const stg = lbase + wave * 32 * kStRow;
-      float* const orow0 = o_part + (slot * kH + wave * 32) * kDc;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < 2; ++half) {  // head block: own, then the partner's
+        float* const orow0 = o_part + (slot * kH + (half ? wave ^ 1 : wave) * 32) * kDc + 256 * lh;
+        const float inv = half ? inv_peer : inv_own;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const f32x16 v = acc[8 * half + m] * inv;
+          const f32x16 v = acc[2 * m + half] * inv;
 #pragma unroll
           for (int j4 = 0; j4 < 4; ++j4) {
             const u32x4 f = {__float_as_uint(v[4 * j4]), __float_as_uint(v[4 * j4 + 1]), __float_as_uint(v[4 * j4 + 2]),
@@ -516,7 +559,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
 #pragma unroll 8
         for (int r = 0; r < 32; ++r) {
           const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stg + r * kStRow + 16 * lane);
-          *reinterpret_cast<u32x4*>(orow0 + size_t(r) * kDc + 256 * half + 4 * lane) = x;
+          *reinterpret_cast<u32x4*>(orow0 + size_t(r) * kDc + 4 * lane) = x;
         }
       }
     }
