@@ -189,6 +189,91 @@ def bench_prefill(args, w) -> dict:
     return rec
 
 
+def cpu_baseline_kv_append(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle's cache-write steps on rows of the same workload until `seconds` pass."""
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = inp["dtype"]
+    w_dkv, w_kr = gen.as_f64(inp["w_dkv"], dt), gen.as_f64(inp["w_kr"], dt)
+    n = 0
+    t0 = time.perf_counter()
+    while n < inp["h"].shape[0]:
+        h = gen.as_f64(inp["h"][n:n + 1], dt)
+        O.cache_rows(O.rms_normalize(O.kv_latent(h, w_dkv), gen.RMS_EPS),
+                     O.rope_key(h, w_kr, inp["positions"][n:n + 1], w.rope_base))
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    nbytes = _kv_append_bytes(w, n)
+    return {"value": round(nbytes / el / 1e9, 6), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {inp['h'].shape[0]} new rows (fp64 NumPy; algorithmic bytes counted) "
+                      f"in {el:.1f} s"}
+
+
+def _kv_append_bytes(w, rows: int) -> int:
+    """Algorithmic HBM bytes of one cache write: both weight matrices, the new hidden states, the
+    written rows (bf16) and the row addresses."""
+    return 2 * w.d_model * (w.d_c + w.d_r) + 2 * rows * w.d_model + rows * 2 * (w.d_c + w.d_r) + 8 * rows
+
+
+def bench_kv_append(args, w) -> dict:
+    """Cache write of new tokens: mla_kv_append per step (weight-read bound at decode batch)."""
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_31_amd as M
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    inp = gen.make_kv_append_inputs(w)
+    dev = torch.device("cuda:0")
+    to = lambda a: runner.to_device(a, dev)  # noqa: E731
+    R = inp["h"].shape[0]
+    d = runner.dims_for(w)
+    pool, table = to(inp["pool"]), to(inp["page_table"])
+    c = M.cache(pool, table, to(np.zeros(w.batch, np.int32)))
+    h, w_dkv, w_kr = to(inp["h"]), to(inp["w_dkv"]), to(inp["w_kr"])
+    seq, pos = to(inp["seq_ids"]), to(inp["positions"])
+    ws_bytes = M.mla_kv_append_workspace_bytes(d, w.d_model, R)
+    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device=dev)
+
+    def step():
+        M.mla_kv_append(d, c, w.d_model, h, w_dkv, w_kr, seq, pos, R, gen.RMS_EPS, ws, ws_bytes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = _kv_append_bytes(w, R)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "MLA cache-write GB/s (V3 shape, 1 GPU)",
+        "value": round(gbs, 3), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rows": R, "d_model": w.d_model, "d_c": w.d_c, "d_r": w.d_r,
+                   "page_size": w.page_size, "seed": w.seed, "workspace_bytes": ws_bytes,
+                   "kv_append_kernel": "mfma" if ws_bytes > 0 else "generic"},
+        "rows_per_s": round(R / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "mla_kv_append (both launches)", "achieved": round(gbs, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "ms_per_launch": round(ms, 6), "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_kv_append(inp, min(args.cpu_seconds, 5.0))
+    return rec
+
+
 COPY_PROBE_KERNEL = "neg_kernel"  # the calibration copy: torch.neg over a float32 buffer (1 read, 1 write)
 
 
@@ -264,8 +349,11 @@ def main() -> int:
     if w.kind == "prefill":
         print(json.dumps(bench_prefill(args, w)), flush=True)
         return 0
+    if w.kind == "kv_append":
+        print(json.dumps(bench_kv_append(args, w)), flush=True)
+        return 0
     if w.kind != "decode":
-        print(f"workload {w.name} is neither a decode nor a prefill workload", file=sys.stderr)
+        print(f"workload {w.name} is not a decode, prefill or cache-write workload", file=sys.stderr)
         return 2
     inp = gen.make_decode_inputs(w)
     dev = torch.device("cuda:0")

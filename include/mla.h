@@ -194,14 +194,23 @@ mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq
 
 /* Cache write for new tokens ([molayo] formal definition, compression; [huny] section 2,
  * decoupled RoPE; [ase] Fig. 1 note on the latent norm):
- *   c = h . W_DKV, optionally RMS-normalised (unit gain) when rms_eps > 0;
+ *   c = h . W_DKV, optionally RMS-normalised (unit gain) when rms_eps > 0:
+ *       c / sqrt(mean(c^2) + rms_eps) over the d_c latent values;
  *   k^R = RoPE_{pos}(h . W_KR); row [c | k^R] stored at token `positions[r]` of sequence
- *   `seq_ids[r]` through the page table of `cache` (cache->pool is written).
+ *   `seq_ids[r]` through the page table of `cache` (cache->pool is written; no other row is).
  *   h device dtype [rows, d_model]; w_dkv dtype [d_model, d_c]; w_kr dtype [d_model, d_r]
- *   seq_ids, positions device int32 [rows]                                                       */
+ *   seq_ids, positions device int32 [rows]; two rows must not name the same token.
+ *   workspace: device fp32 scratch of at least mla_kv_append_workspace_bytes(dims, d_model, rows)
+ *   bytes, owned by the caller, contents ignored and overwritten (NULL allowed when that size
+ *   is 0).  A smaller workspace_bytes gives MLA_ERR_SHAPE.
+ * bf16 with d_c 512, d_r 64 and d_model a multiple of 256 runs on MFMA (a split-K product into
+ * the workspace, then one wave per row for the norm, the rotation and the store); every other
+ * shape runs the generic kernel, which needs no workspace. */
+size_t mla_kv_append_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows);
 mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
                          const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
-                         const int32_t* positions, int32_t rows, float rms_eps, void* stream);
+                         const int32_t* positions, int32_t rows, float rms_eps, float* workspace,
+                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,7 @@ from ._lib import (  # noqa: F401
     mla_decode_partial_balanced,
     mla_decode_uses_mfma,
     mla_kv_append,
+    mla_kv_append_workspace_bytes,
     mla_out_proj,
     mla_prefill_chunk,
     mla_prefill_uses_mfma,

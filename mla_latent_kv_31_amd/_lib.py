@@ -69,7 +69,8 @@ _SIGNATURES = {
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
-    "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP]),
+    "mla_kv_append_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
+    "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
 }
 
 
@@ -203,8 +204,13 @@ def mla_project_query(d: MlaDims, d_model: int, d_cq: int, h, w_dq, w_uq, w_qr, 
            "mla_project_query")
 
 
+def mla_kv_append_workspace_bytes(d: MlaDims, d_model: int, rows: int) -> int:
+    return int(library().mla_kv_append_workspace_bytes(ctypes.byref(d), d_model, rows))
+
+
 def mla_kv_append(d: MlaDims, c: MlaCache, d_model: int, h, w_dkv, w_kr, seq_ids, positions, rows: int,
-                  rms_eps: float = 0.0, stream=None) -> None:
+                  rms_eps: float = 0.0, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     _check(library().mla_kv_append(ctypes.byref(d), ctypes.byref(c), d_model, _addr(h), _addr(w_dkv), _addr(w_kr),
-                                   _addr(seq_ids), _addr(positions), rows, rms_eps, _stream(stream)),
+                                   _addr(seq_ids), _addr(positions), rows, rms_eps, _addr(workspace),
+                                   workspace_bytes, _stream(stream)),
            "mla_kv_append")

@@ -254,21 +254,39 @@ mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq
   return hip_status(launch_project_query(d, d_model, d_cq, h, w_dq, w_uq, w_qr, rows, q_c, q_r, (hipStream_t)stream));
 }
 
+static bool kv_append_uses_mfma(const mla_dims* dims, const Dims& d, int32_t d_model) {
+  return !(dims->flags & MLA_FLAG_FORCE_GENERIC) && kv_append_mfma_supported(d, d_model);
+}
+
+size_t mla_kv_append_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows) {
+  Dims d;
+  if (check_dims(dims, &d) != MLA_OK || d_model < 1 || rows < 1) return 0;
+  return kv_append_uses_mfma(dims, d, d_model) ? kv_append_mfma_workspace(d_model, rows) : 0;
+}
+
 mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
                          const void* w_dkv, const void* w_kr, const int32_t* seq_ids, const int32_t* positions,
-                         int32_t rows, float rms_eps, void* stream) {
+                         int32_t rows, float rms_eps, float* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   Cache c;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   if (d_model < 1 || rows < 0 || !(rms_eps == rms_eps)) return MLA_ERR_SHAPE;
-  if (d_model + d.dc + d.dr > 8192) return MLA_ERR_UNSUPPORTED;
+  const bool mfma = kv_append_uses_mfma(dims, d, d_model);
+  if (!mfma && d_model + d.dc + d.dr > 8192) return MLA_ERR_UNSUPPORTED;
+  if (mfma && int64_t(rows) * d_model > (int64_t(1) << 31) - 1) return MLA_ERR_UNSUPPORTED;
   MLA_TRY(ptr_ok(h));
   MLA_TRY(ptr_ok(w_dkv));
   if (d.dr > 0) MLA_TRY(ptr_ok(w_kr));
   MLA_TRY(ptr_ok(seq_ids));
   MLA_TRY(ptr_ok(positions));
   if (rows == 0) return MLA_OK;
+  if (mfma) {
+    MLA_TRY(ptr_ok(workspace));
+    if (workspace_bytes < kv_append_mfma_workspace(d_model, rows)) return MLA_ERR_SHAPE;
+    return hip_status(launch_kv_append_mfma(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps,
+                                            workspace, (hipStream_t)stream));
+  }
   return hip_status(
       launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
 }

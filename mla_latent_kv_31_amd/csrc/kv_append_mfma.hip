@@ -1,0 +1,242 @@
+// Cache write for new tokens on bf16 MFMA (gfx950), DeepSeek-V3 latent shape (d_c 512, d_r 64).
+//
+// For each new token r ([molayo] formal definition, KV compression; [huny] section 2, decoupled
+// RoPE; [ase] Fig. 1 note on the norm that follows the latent):
+//   y = h_r . [W_DKV | W_KR]                      (576 wide, fp32 accumulate)
+//   c = y[0:512], RMS-normalised with unit gain when rms_eps > 0
+//   k^R = RoPE_{pos_r}(y[512:576]), interleaved pairs, inverse frequencies base^(-2i/64)
+//   pool row of (seq_ids[r], positions[r]) = bf16([c | k^R])
+//
+// Two launches.  The product is a skinny GEMM (rows x d_model) . (d_model x 576) that is bound by
+// reading the weights at decode batch sizes, so its K range is split over enough workgroups to
+// keep every CU streaming: kv_gemm_kernel writes fp32 partial products [split][row][576] to the
+// caller's workspace.  kv_finish_kernel (one workgroup per row, its four waves sharing the splits)
+// sums the splits, normalises, rotates, rounds to bf16 and stores the 1,152-byte row through the
+// page table.
+//
+// kv_gemm_kernel: a workgroup of two waves computes a 64-row x 32-column tile over its K range,
+// wave w rows 32w..32w+31, with v_mfma_f32_32x32x16_bf16.  A operand (h) comes straight from
+// global memory, 16 bytes per lane (row l%32, k 8*(l/32)..+7 of the k-step).  The weight slice
+// [256 k x 32 columns] is staged in LDS per chunk (row-major, 64-byte rows) and read with
+// ds_read_b64_tr_b16: lane i of each 16-lane group receives column i of the 4 x 16 block the
+// group addresses, which is the B-operand layout (column l%32, k 8*(l/32)..+7) in two reads.
+
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr int kDc = 512, kDr = 64, kW = kDc + kDr;
+constexpr int kCols = 32;             // output columns per workgroup
+constexpr int kColTiles = kW / kCols; // 18
+constexpr int kRowsWg = 64;           // output rows per workgroup (two waves)
+constexpr int kChunk = 256;           // k rows of the weight slice staged per LDS chunk
+constexpr int kThreads = 128;
+constexpr int kChunkB = kChunk * kCols * 2;          // 16 KiB
+constexpr int kLoadsPerThread = kChunkB / 16 / kThreads;  // 8 x 16 B
+
+__global__ __launch_bounds__(kThreads) void kv_gemm_kernel(const uint16_t* __restrict__ h, int d_model, int rows,
+                                                          const uint16_t* __restrict__ w_dkv,
+                                                          const uint16_t* __restrict__ w_kr, int k_per_split,
+                                                          float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kChunkB];
+  lds_u8* const lbase = (lds_u8*)smem;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ct = blockIdx.x, rt = blockIdx.y, ks = blockIdx.z;
+  const int col0 = ct * kCols;
+  // the weight slice: columns col0..col0+31 of W_DKV, or of W_KR for the last two tiles
+  const uint16_t* wsrc = col0 < kDc ? w_dkv + col0 : w_kr + (col0 - kDc);
+  const int wstride = col0 < kDc ? kDc : kDr;
+  const int k_begin = ks * k_per_split;
+  const int nchunks = k_per_split / kChunk;
+
+  // A operand rows (clamped: rows past the end compute garbage that is never stored)
+  const int row = min(rt * kRowsWg + wave * 32 + (lane & 31), rows - 1);
+  const uint16_t* hrow = h + size_t(row) * d_model + 8 * (lane >> 5);
+
+  // cooperative staging of one chunk: thread t moves 16-byte pieces t + 128 x of the slice,
+  // piece p = (k row p / 4, quarter p % 4 of its 64 bytes)
+  u32x4 stage[kLoadsPerThread];
+  auto load_chunk = [&](int c) {
+    const int k0 = k_begin + c * kChunk;
+#pragma unroll
+    for (int x = 0; x < kLoadsPerThread; ++x) {
+      const int p = threadIdx.x + kThreads * x;
+      stage[x] = *reinterpret_cast<const u32x4*>(wsrc + size_t(k0 + (p >> 2)) * wstride + 8 * (p & 3));
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < kLoadsPerThread; ++x) {
+      const int p = threadIdx.x + kThreads * x;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + buf * kChunkB + 16 * p) = stage[x];
+    }
+  };
+  // transposing reads: group g = lane/16 addresses k rows 8*(g/2) + 4*half + (lane%16)/4 and
+  // columns 16*(g%2) + 4*(lane%4) .. +3 of a 16-row k-step
+  const int g = lane >> 4, i16 = lane & 15;
+  const int tr_off = (8 * (g >> 1) + (i16 >> 2)) * (kCols * 2) + 2 * (16 * (g & 1) + 4 * (i16 & 3));
+
+  f32x16 acc;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) acc[x] = 0.f;
+
+  // A operands of one chunk: 16 k-steps, 16 bytes per lane each
+  bf16x8 a[kChunk / 16], a_next[kChunk / 16];
+  auto load_a = [&](bf16x8* dst, int c) {
+    const int k0 = k_begin + c * kChunk;
+#pragma unroll
+    for (int s = 0; s < kChunk / 16; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(hrow + k0 + 16 * s);
+  };
+  load_a(a, 0);
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    // the next chunk's operands are in flight while this one is multiplied (issued after this
+    // chunk's A loads, so the in-order wait counts only wait for what the MFMAs use)
+    if (c + 1 < nchunks) {
+      load_a(a_next, c + 1);
+      load_chunk(c + 1);
+    }
+    const lds_u8* wb = lbase + buf * kChunkB + tr_off;
+#pragma unroll
+    for (int s = 0; s < kChunk / 16; ++s) {
+      const lds_u8* p = wb + s * 16 * (kCols * 2);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(p + 4 * (kCols * 2)));
+      const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b, acc, 0, 0, 0);
+    }
+    if (c + 1 < nchunks) {
+      store_chunk(buf ^ 1);  // that buffer was last read before the previous barrier
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kChunk / 16; ++s) a[s] = a_next[s];
+    }
+  }
+
+  // D layout: column l%32, rows 8*(x/4) + 4*(l/32) + x%4
+  float* const out = part + (size_t(ks) * rows) * kW + col0 + (lane & 31);
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int r = rt * kRowsWg + wave * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+    if (r < rows) out[size_t(r) * kW] = acc[x];
+  }
+}
+
+// RoPE inverse frequencies base^(-2i/d_r), computed on the host in double.
+struct InvFreq {
+  double v[kDr / 2];
+};
+
+constexpr int kFinishWaves = 4;  // waves per row in the finish: they share out the K splits
+
+__global__ __launch_bounds__(64 * kFinishWaves) void kv_finish_kernel(const float* __restrict__ part, int rows,
+                                                                     int splits, Cache c,
+                                                                     const int32_t* __restrict__ seq_ids,
+                                                                     const int32_t* __restrict__ positions,
+                                                                     float rms_eps, InvFreq inv_freq) {
+  __shared__ float red[kFinishWaves - 1][10][64];
+  const int r = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // lane: latent columns 8*lane .. +7 and, for lane < 32, rotary pair lane; wave q sums the splits
+  // q, q+4, ... (unrolled, so the loads of several splits are in flight together), then wave 0
+  // adds the other waves' sums
+  float v[10] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = wave; s < splits; s += kFinishWaves) {
+    const float* p = part + (size_t(s) * rows + r) * kW;
+    const float4 x0 = *reinterpret_cast<const float4*>(p + 8 * lane);
+    const float4 x1 = *reinterpret_cast<const float4*>(p + 8 * lane + 4);
+    const float2 y = *reinterpret_cast<const float2*>(p + kDc + 2 * (lane & 31));
+    v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+    v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+    v[8] += y.x; v[9] += y.y;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int x = 0; x < 10; ++x) red[wave - 1][x][lane] = v[x];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int q = 0; q < kFinishWaves - 1; ++q)
+#pragma unroll
+    for (int x = 0; x < 10; ++x) v[x] += red[q][x][lane];
+  const float k1 = v[8], k2 = v[9];
+  float ss = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) ss = fmaf(v[x], v[x], ss);
+  ss = wave_sum(ss);
+  const float scale = rms_eps > 0.f ? 1.f / sqrtf(ss / float(kDc) + rms_eps) : 1.f;
+
+  const int b = seq_ids[r], t = positions[r];
+  uint16_t* row = const_cast<uint16_t*>(static_cast<const uint16_t*>(c.pool)) +
+                  row_index(c.page_table, c.max_pages, c.page_size, b, t) * kW;
+  u32x4 o;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    o[x] = uint32_t(f32_to_bf16(v[2 * x] * scale)) | (uint32_t(f32_to_bf16(v[2 * x + 1] * scale)) << 16);
+  *reinterpret_cast<u32x4*>(row + 8 * lane) = o;
+  if (lane < kDr / 2) {
+    // angle pos * base^(-2i/d_r), i = lane, in double, reduced to [-pi, pi] before the float32
+    // sine and cosine
+    const double ang = double(t) * inv_freq.v[lane];
+    const double rd = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, cn;
+    sincosf(float(rd), &sn, &cn);
+    const float r1 = k1 * cn - k2 * sn, r2 = k1 * sn + k2 * cn;
+    *reinterpret_cast<uint32_t*>(row + kDc + 2 * lane) = uint32_t(f32_to_bf16(r1)) | (uint32_t(f32_to_bf16(r2)) << 16);
+  }
+}
+
+// K splits for `rows` new tokens: enough workgroups (about two per CU) to keep every CU
+// streaming weights, each split a whole number of 256-row chunks.
+int kv_splits(int d_model, int rows) {
+  const int nchunk = d_model / kChunk;
+  const int tiles = kColTiles * ((rows + kRowsWg - 1) / kRowsWg);
+  const int want = max(1, (512 + tiles - 1) / tiles);
+  int best = 1;
+  for (int s = 1; s <= nchunk; ++s)
+    if (nchunk % s == 0 && s <= want) best = s;
+  return best;
+}
+
+}  // namespace
+
+bool kv_append_mfma_supported(const Dims& d, int d_model) {
+  return d.dtype == MLA_BF16 && d.dc == kDc && d.dr == kDr && d_model >= kChunk && d_model % kChunk == 0;
+}
+
+size_t kv_append_mfma_workspace(int d_model, int rows) {
+  return size_t(kv_splits(d_model, rows)) * size_t(rows) * kW * sizeof(float);
+}
+
+hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
+                                 const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
+                                 float rms_eps, float* workspace, hipStream_t s) {
+  const int splits = kv_splits(d_model, rows);
+  const dim3 grid(kColTiles, (rows + kRowsWg - 1) / kRowsWg, splits);
+  kv_gemm_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(h), d_model, rows,
+                                           static_cast<const uint16_t*>(w_dkv), static_cast<const uint16_t*>(w_kr),
+                                           d_model / splits, workspace);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  InvFreq inv;
+  for (int i = 0; i < kDr / 2; ++i) inv.v[i] = pow(double(d.rope_base), -2.0 * i / kDr);
+  kv_finish_kernel<<<rows, 64 * kFinishWaves, 0, s>>>(workspace, rows, splits, c, seq_ids, positions, rms_eps, inv);
+  return hipGetLastError();
+}
+
+}  // namespace mla

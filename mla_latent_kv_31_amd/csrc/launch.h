@@ -69,6 +69,12 @@ hipError_t launch_out_proj_generic(const Dims& d, const float* z, const void* w_
 hipError_t launch_project_query(const Dims& d, int d_model, int d_cq, const void* h, const void* w_dq,
                                 const void* w_uq, const void* w_qr, int rows, void* q_c, void* q_r,
                                 hipStream_t s);
+// ---- bf16 MFMA cache write for the DeepSeek-V3 latent shape (d_c 512, d_r 64, d_model % 256 == 0)
+bool kv_append_mfma_supported(const Dims& d, int d_model);
+size_t kv_append_mfma_workspace(int d_model, int rows);
+hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
+                                 const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
+                                 float rms_eps, float* workspace, hipStream_t s);
 hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                             const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                             float rms_eps, hipStream_t s);

@@ -55,7 +55,7 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 class Workload:
     name: str
     seed: int
-    kind: str                       # "toy" | "decode" | "prefill"
+    kind: str                       # "toy" | "decode" | "prefill" | "kv_append"
     batch: int
     n_heads: int = 128
     d_c: int = 512
@@ -70,7 +70,7 @@ class Workload:
     split_tokens: int = 0           # split-K chunk length used when this workload is timed
     q_len: int = 1                  # query tokens per sequence (prefill chunk length)
     rope_base: float = 10000.0
-    d_model: int = 0                # toy only: hidden width
+    d_model: int = 0                # hidden width (toy and cache-write workloads)
     d_cq: int = 0                   # toy only: query-latent width
     notes: str = field(default="", compare=False)
 
@@ -101,9 +101,19 @@ WORKLOADS: dict[str, Workload] = {
     "v3_prefill_b2": Workload(
         name="v3_prefill_b2", seed=5, kind="prefill", batch=2, ctx=2048, q_len=512,
         notes="2,048 prior tokens + a 512-token causal chunk already appended to the cache"),
+    # cache-write workloads: d_model 4096 is the hidden width of the [molayo] implementation code
+    "v3_kv_append_b64": Workload(
+        name="v3_kv_append_b64", seed=6, kind="kv_append", batch=64, ctx_range=(1024, 32768), q_len=1,
+        random_pages=True, d_model=4096,
+        notes="one new token per sequence of the ragged decode batch, written at position len-1"),
+    "v3_kv_append_prefill_b2": Workload(
+        name="v3_kv_append_prefill_b2", seed=7, kind="kv_append", batch=2, ctx=2048, q_len=512,
+        random_pages=True, d_model=4096,
+        notes="the 512-token chunk of each of 2 sequences, written at positions 2048..2559"),
 }
 
-WORKLOAD_ORDER = ["toy_fp32", "v3_b1_ctx4k", "v3_b64_ragged_paged", "v3_b4_ctx128k", "v3_prefill_b2"]
+WORKLOAD_ORDER = ["toy_fp32", "v3_b1_ctx4k", "v3_b64_ragged_paged", "v3_b4_ctx128k", "v3_prefill_b2",
+                  "v3_kv_append_b64", "v3_kv_append_prefill_b2"]
 
 
 # --------------------------------------------------------------------------
@@ -272,6 +282,47 @@ def make_toy_inputs(w: Workload | None = None, *, seed: int | None = None) -> di
     out["w_kr"] = _normal(rng, (d, w.d_r))
     out["pos"] = np.arange(L, dtype=np.int32)
     return out
+
+
+def make_kv_append_inputs(w: Workload, *, seed: int | None = None, rows: int | None = None,
+                          fill: str = "random", spare_pages: int = 4) -> dict:
+    """Inputs for one cache write of new tokens.
+
+    Sequence b receives q_len new tokens at positions p0_b .. p0_b + q_len - 1, where p0_b =
+    len_b - 1 for ragged decode workloads (len_b drawn like the decode batch) and ctx otherwise.
+    Only the pages that hold new tokens exist: distinct physical pages in seeded random order,
+    every other table entry -1.  The pool starts filled with `fill` values.
+    Draw order: lengths, W_DKV, W_KR (both N(0,1)/sqrt(d_model), d_model their fan-in), h
+    (N(0,1)), page permutation, fills.  `rows` truncates the token list (edge cases).
+    Returns h [R, d_model], w_dkv [d_model, d_c], w_kr [d_model, d_r], seq_ids [R], positions [R],
+    pool [P, page, d_c+d_r], page_table [B, max_pages].
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    if w.ctx_range is not None:
+        p0 = draw_lengths(w, rng) - 1
+    else:
+        p0 = np.full(w.batch, w.ctx, dtype=np.int32)
+    d = w.d_model
+    w_dkv = _normal(rng, (d, w.d_c), 1.0 / math.sqrt(d))
+    w_kr = _normal(rng, (d, w.d_r), 1.0 / math.sqrt(d))
+    seq_ids = np.repeat(np.arange(w.batch, dtype=np.int32), w.q_len)
+    positions = (p0[:, None] + np.arange(w.q_len, dtype=np.int32)[None]).reshape(-1).astype(np.int32)
+    if rows is not None:
+        seq_ids, positions = seq_ids[:rows], positions[:rows]
+    R = seq_ids.shape[0]
+    h = _normal(rng, (R, d))
+    ps = w.page_size
+    need = sorted({(int(b), int(t) // ps) for b, t in zip(seq_ids, positions)})
+    total = len(need) + spare_pages
+    order = rng.permutation(total) if w.random_pages else np.arange(total)
+    max_pages = max(int(t) // ps for t in positions) + 1
+    table = np.full((w.batch, max_pages), -1, dtype=np.int32)
+    for k, (b, lp) in enumerate(need):
+        table[b, lp] = int(order[k])
+    pool = _fill_values(rng, (total, ps, w.row_width), fill, w.dtype)
+    return dict(workload=w, dtype=w.dtype, h=_store(h, w.dtype), w_dkv=_store(w_dkv, w.dtype),
+                w_kr=_store(w_kr, w.dtype), seq_ids=seq_ids, positions=positions, pool=pool,
+                page_table=table)
 
 
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:

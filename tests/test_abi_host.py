@@ -124,8 +124,9 @@ def test_other_entry_points_validation():
     assert lib.mla_prefill_chunk(ctypes.byref(d), ctypes.byref(c), A, 0, A, A, None, None) == M.MLA_OK
     assert lib.mla_project_query(ctypes.byref(d), 0, 3, A, A, A, A, 1, A, A, None) == M.MLA_ERR_SHAPE
     assert lib.mla_project_query(ctypes.byref(d), 8, 3, A, A, A, None, 1, A, A, None) == M.MLA_ERR_NULL
-    assert lib.mla_kv_append(ctypes.byref(d), ctypes.byref(c), 8, A, A, A, A, None, 1, 0.0, None) == M.MLA_ERR_NULL
-    assert lib.mla_kv_append(ctypes.byref(d), ctypes.byref(c), 8, A, A, A, A, A, 0, 0.0, None) == M.MLA_OK
+    assert lib.mla_kv_append(ctypes.byref(d), ctypes.byref(c), 8, A, A, A, A, None, 1, 0.0, None, 0,
+                             None) == M.MLA_ERR_NULL
+    assert lib.mla_kv_append(ctypes.byref(d), ctypes.byref(c), 8, A, A, A, A, A, 0, 0.0, None, 0, None) == M.MLA_OK
 
 
 def test_binding_refuses_host_tensors():

@@ -47,7 +47,7 @@ def test_toy_single_step_end_to_end(page_size, split):
     lens = dev(np.array([Lc], np.int32))
     c = M.cache(pool, table, lens)
     M.mla_kv_append(d, c, w.d_model, h, dev(t["w_dkv"]), dev(t["w_kr"]), dev(np.zeros(Lc, np.int32)),
-                    dev(np.arange(Lc, dtype=np.int32)), Lc, 0.0)
+                    dev(np.arange(Lc, dtype=np.int32)), Lc, 0.0, None, 0)
     q_c = torch.empty((1, w.n_heads, w.d_k), device=DEV)
     q_r = torch.empty((1, w.n_heads, w.d_r), device=DEV)
     M.mla_project_query(d, w.d_model, w.d_cq, h[Lc - 1:Lc], dev(t["w_dq"]), dev(t["w_uq"]), dev(t["w_qr"]), 1, q_c, q_r)
