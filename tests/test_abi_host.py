@@ -163,3 +163,25 @@ def test_balanced_validation():
     assert comb(_cache(), z=None) == M.MLA_ERR_NULL
     assert comb(_cache(), lse=U) == M.MLA_ERR_ALIGN
     assert comb(_cache(batch=0)) == M.MLA_OK
+
+
+def test_kv_append_workspace_validation():
+    """The MFMA cache write needs a caller workspace of the advertised size; other shapes need none."""
+    lib = M.library()
+    d = _dims()
+    need = M.mla_kv_append_workspace_bytes(d, 4096, 64)
+    assert need == 16 * 64 * 576 * 4  # 16 K splits for a 64-row decode batch
+    assert M.mla_kv_append_workspace_bytes(d, 4096, 1024) == 2 * 1024 * 576 * 4
+    assert M.mla_kv_append_workspace_bytes(d, 4000, 64) == 0  # d_model not a multiple of 256: generic
+    assert M.mla_kv_append_workspace_bytes(_dims(dtype=M.MLA_F32), 4096, 64) == 0
+    assert M.mla_kv_append_workspace_bytes(_dims(flags=M.MLA_FLAG_FORCE_GENERIC), 4096, 64) == 0
+    assert M.mla_kv_append_workspace_bytes(d, 4096, 0) == 0
+
+    def call(ws=A, nbytes=need, rows=64):
+        return lib.mla_kv_append(ctypes.byref(d), ctypes.byref(_cache()), 4096, A, A, A, A, A, rows, 1e-6, ws,
+                                 nbytes, None)
+
+    assert call(ws=None) == M.MLA_ERR_NULL
+    assert call(nbytes=need - 4) == M.MLA_ERR_SHAPE
+    assert call(ws=U) == M.MLA_ERR_ALIGN
+    assert call(rows=0, ws=None, nbytes=0) == M.MLA_OK
