@@ -11,9 +11,11 @@
 // mla_out_proj ([ase] "Value 투영을 가중합 뒤로 옮기기", Fig. 4 equation):
 //   out[r,h,v] = sum_j z[r,h,j] W_UV[h,j,v]
 // computed as out^T = W_UV[h]^T . z^T.  The contraction runs over j, the row index of W_UV, so
-// the workgroup stages its 512 x 64 slice of W_UV in LDS and reads the A operand with the
-// transposing ds_read_b64_tr_b16; one workgroup per (head, 64 value columns, 128 rows).  z is float32: it is split into bf16 hi + lo parts and both are
-// multiplied (two MFMAs), which keeps the product at float32-level accuracy.
+// the A operand comes from W_UV staged in LDS through the transposing ds_read_b64_tr_b16; the
+// four waves of a workgroup split j.  Up to 256 rows: one workgroup per (head, 64 value columns,
+// 32 or 64 rows); beyond that one workgroup per (head, 64 value columns) streams every row slice.
+// z is float32: it is split into bf16 hi + lo parts and both are multiplied (two MFMAs), which
+// keeps the product at float32-level accuracy.
 
 #include <math.h>
 
@@ -29,6 +31,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDc = 512, kDk = 128, kDv = 128;
 constexpr int kMaxDr = 64;   // the absorb output tile: 64 rows x (512 + 64) bf16 = 72 KiB of LDS
@@ -54,13 +57,18 @@ __host__ inline int xcd_grid(int per_head, int H) { return 8 * ((H + 7) / 8) * p
 // (RB = 1 for small batches, so that a decode step still spreads over every compute unit).
 // The 64 x (d_c + d_r) bf16 output tile, rotary columns included, is assembled in LDS and then
 // written as whole contiguous rows of q_hat (64 x 16 B per store instruction).
+// RoPE inverse frequencies base^(-2i/d_r), computed on the host in double (kernel argument).
+struct RopeFreq {
+  double v[kMaxDr / 2];
+};
+
 template <int RB>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, float rope_base, float qscale,
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, RopeFreq inv_freq, float qscale,
                                                           const uint16_t* __restrict__ q_c,
                                                           const uint16_t* __restrict__ q_r,
                                                           const uint16_t* __restrict__ w_uk,
                                                           const int32_t* __restrict__ pos, uint16_t* __restrict__ q_hat) {
-  __shared__ __attribute__((aligned(16))) unsigned char ab_smem[32 * RB * (kDc + kMaxDr + 8) * 2 + kMaxDr / 2 * 8];
+  __shared__ __attribute__((aligned(16))) unsigned char ab_smem[32 * RB * (kDc + kMaxDr + 8) * 2];
   constexpr int kRows = 32 * RB;
   const int slices = (R + kRows - 1) / kRows;
   int h, rs;
@@ -73,9 +81,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
   typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_u16* const tile = (lds_u16*)ab_smem;
-  __attribute__((address_space(3))) double* const inv_freq =
-      (__attribute__((address_space(3))) double*)(ab_smem + kRows * TW * 2);
-  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) inv_freq[i] = pow(double(rope_base), -2.0 * i / dr);
+  __shared__ double freq[kMaxDr / 2];  // per-lane indexing of the kernel argument would be a load per use
 
   // B operands: both row blocks of q_c, loaded once
   bf16x8 bq[RB][kDk / 16];
@@ -86,6 +92,21 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) bq[rb][ks] = r < R ? load_bf16x8(qrow + 16 * ks) : bf16x8{};
   }
+  // rotary inputs: thread t handles (row, 4 pairs) items t and t + 256 (at most RB of them), loaded
+  // here with everything else so that the workgroup waits for memory once
+  const int quads = dr / 8;  // dr is a multiple of 8 here
+  u32x4 rin[RB];
+  int rpos[RB];
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    const int idx = threadIdx.x + 256 * t, rr = idx / max(quads, 1), qd = idx - rr * max(quads, 1);
+    const bool ok = idx < nrows * quads;
+    const int r = ok ? r0 + rr : r0;
+    rin[t] = ok ? *reinterpret_cast<const u32x4*>(q_r + (size_t(r) * H + h) * dr + 8 * qd) : u32x4{0u, 0u, 0u, 0u};
+    rpos[t] = ok ? pos[r] : 0;
+  }
+  double fr = 0.0;  // the frequency table entry this thread stages in LDS
+  if (threadIdx.x < kMaxDr / 2) fr = inv_freq.v[threadIdx.x];
   // A operands of all four column blocks, loaded together with the B operands so that the wave
   // waits for memory once
   const uint16_t* wbase = w_uk + (size_t(h) * kDc + 128 * wave + (lane & 31)) * kDk + 8 * hi;
@@ -94,6 +115,18 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) a[jb][ks] = load_bf16x8(wbase + size_t(32 * jb) * kDk + 16 * ks);
+  // an empty asm that reads every loaded value: the compiler would otherwise move loads next to
+  // their uses and put several memory latencies in a row on the critical path
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int ks = 0; ks < kDk / 16; ++ks) asm volatile("" : "+v"(a[jb][ks]));
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int ks = 0; ks < kDk / 16; ++ks) asm volatile("" : "+v"(bq[rb][ks]));
+    asm volatile("" : "+v"(rin[rb]), "+v"(rpos[rb]));
+  }
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
     f32x16 acc[RB];
@@ -121,19 +154,22 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
       }
     }
   }
-  __syncthreads();  // inv_freq ready
-  // rotary columns: one thread per (row, 4 pairs) with 16-byte loads of q_r
-  const int quads = dr / 8;  // dr is a multiple of 8 here
-  for (int idx = threadIdx.x; idx < nrows * quads; idx += blockDim.x) {
-    const int rr = idx / quads, qd = idx % quads, r = r0 + rr;
-    const u32x4 in = *reinterpret_cast<const u32x4*>(q_r + (size_t(r) * H + h) * dr + 8 * qd);
-    const double p = double(pos[r]);
+  if (threadIdx.x < kMaxDr / 2) freq[threadIdx.x] = fr;
+  __syncthreads();  // the frequency table is visible to every wave
+  // rotary columns
+#pragma unroll
+  for (int t = 0; t < RB; ++t) {
+    const int idx = threadIdx.x + 256 * t;
+    if (idx >= nrows * quads) break;
+    const int rr = idx / quads, qd = idx - rr * quads;
+    const u32x4 in = rin[t];
+    const double p = double(rpos[t]);
     u32x4 outv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = 4 * qd + k;
       // angle in double, reduced to [-pi, pi] before the float32 sine/cosine
-      const double ang = p * inv_freq[i];
+      const double ang = p * freq[i];
       const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
       float sn, cs;
       sincosf(float(red), &sn, &cs);
@@ -156,16 +192,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 // ---------------------------------------------------------------------------------------- out_proj
 constexpr int kOpCols = 64;                    // v columns per workgroup
 constexpr int kOpRowB = kOpCols * 2;           // 128 bytes per W row slice in LDS
-constexpr int kOpLds = kDc * kOpRowB;          // 64 KiB
-constexpr int kOpRows = 128;                   // rows per workgroup: 4 blocks of 32, two per wave
+constexpr int kOpJ = kDc / 4;                  // j rows (contraction) per wave
+constexpr int kOpWaveB = kOpJ * kOpRowB;       // 16 KiB: a wave's W slice, later its partial sums
 
 // LDS place of 16-byte chunk c (0..7) of W row j: rows j and j+2 sit half a row apart, so that
 // the 4-row x 64-byte transposing reads cover all 64 banks.
 __device__ __forceinline__ int op_chunk(int j, int c) { return c ^ (((j >> 1) & 1) << 2); }
 
-// z[r][16ks + 8hi .. +7] as a bf16 hi + lo pair (zero for rows past the end)
-__device__ __forceinline__ void split_hilo(float4 z0, float4 z1, bool valid, bf16x8& zh, bf16x8& zl) {
-  const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+// z[r][j .. j+7] as a bf16 hi + lo pair (zero for rows past the end)
+__device__ __forceinline__ void split_hilo(f32x4 z0, f32x4 z1, bool valid, bf16x8& zh, bf16x8& zl) {
+  const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     const float v = valid ? zv[x] : 0.f;
@@ -174,107 +210,226 @@ __device__ __forceinline__ void split_hilo(float4 z0, float4 z1, bool valid, bf1
   }
 }
 
-// 4 waves: wave w owns v block (w & 1) and row blocks (w >> 1) and (w >> 1) + 2 of the
-// workgroup's 128 rows; the two row blocks share every A read.
-template <bool TWO>
-__device__ __forceinline__ void out_proj_rows(const lds_u8* lw, int H, int R, int h, int v0, int vb, int rbA,
-                                              const float* __restrict__ z, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
-  const int rq = ii >> 2, ccol = vb * 32 + 16 * (g & 1) + 4 * (ii & 3);
-  auto tr_addr = [&](int j) -> const lds_u8* {
-    return lw + j * kOpRowB + 16 * op_chunk(j, ccol >> 3) + 2 * (ccol & 7);
-  };
-  const int ra = rbA + (lane & 31), rb = ra + 64;
-  const bool va = ra < R, vbb = TWO && rb < R;
-  const float* za = z + (size_t(va ? ra : 0) * H + h) * kDc + 8 * hi;
-  const float* zb = z + (size_t(vbb ? rb : 0) * H + h) * kDc + 8 * hi;
-  f32x16 acc0, acc1;
-#pragma unroll
-  for (int x = 0; x < 16; ++x) acc0[x] = acc1[x] = 0.f;
-  constexpr int kPre = TWO ? 4 : 8;  // z steps loaded ahead: enough bytes in flight to cover HBM latency
-  float4 ra0[kPre], ra1[kPre], rb0[kPre], rb1[kPre];
-#pragma unroll
-  for (int p = 0; p < kPre; ++p) {
-    ra0[p] = *reinterpret_cast<const float4*>(za + 16 * p);
-    ra1[p] = *reinterpret_cast<const float4*>(za + 16 * p + 4);
-    if (TWO) {
-      rb0[p] = *reinterpret_cast<const float4*>(zb + 16 * p);
-      rb1[p] = *reinterpret_cast<const float4*>(zb + 16 * p + 4);
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < kDc / 16; ++ks) {
-    const int jr = 16 * ks + 8 * (g >> 1) + rq;
-    const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)tr_addr(jr));
-    const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)tr_addr(jr + 4));
-    const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    bf16x8 zh, zl;
-    const int sl = ks % kPre;
-    split_hilo(ra0[sl], ra1[sl], va, zh, zl);
-    if (ks + kPre < kDc / 16) {
-      ra0[sl] = *reinterpret_cast<const float4*>(za + 16 * (ks + kPre));
-      ra1[sl] = *reinterpret_cast<const float4*>(za + 16 * (ks + kPre) + 4);
-    }
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zh, acc0, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zl, acc0, 0, 0, 0);
-    if (TWO) {
-      split_hilo(rb0[sl], rb1[sl], vbb, zh, zl);
-      if (ks + kPre < kDc / 16) {
-        rb0[sl] = *reinterpret_cast<const float4*>(zb + 16 * (ks + kPre));
-        rb1[sl] = *reinterpret_cast<const float4*>(zb + 16 * (ks + kPre) + 4);
-      }
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zh, acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zl, acc1, 0, 0, 0);
-    }
-  }
-  if (va) {
-    float* o = out + (size_t(ra) * H + h) * kDv + v0 + vb * 32 + 4 * hi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(o + 8 * q) = make_float4(acc0[4 * q], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
-  }
-  if (vbb) {
-    float* o = out + (size_t(rb) * H + h) * kDv + v0 + vb * 32 + 4 * hi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(o + 8 * q) = make_float4(acc1[4 * q], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
-  }
-}
-
-// One workgroup per (head, 64 value columns, 128 rows), a head's workgroups on its XCD so that the
-// two column halves of a row slice read the same z rows from that XCD's L2.
+// One workgroup per (head, 64 value columns, 32 * RB rows), a head's workgroups on its XCD so that
+// the two column halves of a row slice read the same z rows from that XCD's L2.  The contraction
+// over j = 0..511 is split across the 4 waves (128 j each).  Every wave issues all its loads at
+// once, its W_UV rows (staged in its own 16 KiB of LDS, which no other wave reads) and its z
+// pieces (16 bytes per lane per k-step and row block), so that a workgroup waits for memory once.
+// The waves' partial sums then meet in LDS: wave w adds up accumulator w of all four.
+template <int RB>
 __global__ __launch_bounds__(256) void out_proj_mfma_kernel(int H, int R, const float* __restrict__ z,
                                                             const uint16_t* __restrict__ w_uv,
                                                             float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kOpLds];
-  lds_u8* const lw = (lds_u8*)smem;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kOpWaveB];
   constexpr int kHalves = kDv / kOpCols;
-  const int slices = (R + kOpRows - 1) / kOpRows;
+  constexpr int kRows = 32 * RB;
+  const int slices = (R + kRows - 1) / kRows;
   int h, inner;
   if (!xcd_head_map(kHalves * slices, H, h, inner)) return;
-  const int v0 = kOpCols * (inner % kHalves), rs = inner / kHalves;
-  const int wave = threadIdx.x >> 6;
-  // stage W_UV[h][:, v0 .. v0+63]: 512 rows x 8 chunks of 16 B, 16 per thread, all loads issued
-  // before the first LDS write
-  constexpr int kPer = kDc * 8 / 256;
+  const int v0 = kOpCols * (inner % kHalves), r0 = kRows * (inner / kHalves);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
+  const int j0 = kOpJ * wave;
+  lds_u8* const lw = (lds_u8*)smem + wave * kOpWaveB;
+
+  // W_UV[h][j0 .. j0+127][v0 .. v0+63]: 128 rows x 8 chunks of 16 B, 16 per lane
+  constexpr int kPer = kOpJ * 8 / 64;
   u32x4 wv[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int c = threadIdx.x + 256 * k, j = c >> 3, ch = c & 7;
-    wv[k] = *reinterpret_cast<const u32x4*>(w_uv + (size_t(h) * kDc + j) * kDv + v0 + 8 * ch);
+    const int c = lane + 64 * k, j = c >> 3, ch = c & 7;
+    wv[k] = *reinterpret_cast<const u32x4*>(w_uv + (size_t(h) * kDc + j0 + j) * kDv + v0 + 8 * ch);
   }
+  // z pieces: row r0 + 32rb + lane%32, j = j0 + 16ks + 8hi .. +7
+  f32x4 zr[RB][kOpJ / 16][2];
+  bool valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = r0 + 32 * rb + (lane & 31);
+    valid[rb] = r < R;
+    const float* zp = z + (size_t(valid[rb] ? r : 0) * H + h) * kDc + j0 + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < kOpJ / 16; ++ks) {
+      zr[rb][ks][0] = *reinterpret_cast<const f32x4*>(zp + 16 * ks);
+      zr[rb][ks][1] = *reinterpret_cast<const f32x4*>(zp + 16 * ks + 4);
+    }
+  }
+  // an empty asm that reads every loaded value keeps the compiler from sinking loads towards their
+  // uses (which would put one memory latency per k-step on the critical path)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < kOpJ / 16; ++ks) asm volatile("" : "+v"(zr[rb][ks][0]), "+v"(zr[rb][ks][1]));
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int c = threadIdx.x + 256 * k, j = c >> 3, ch = c & 7;
+    const int c = lane + 64 * k, j = c >> 3, ch = c & 7;
     *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lw + j * kOpRowB + 16 * op_chunk(j, ch)) = wv[k];
   }
+  // (a wave reads only what it wrote itself: LDS operations of one wave complete in order)
+
+  // out^T[v][r] = W_UV^T[v][j] . z^T[j][r]; A operand by transposing reads: lane group g covers
+  // j rows 8*(g/2) + (lane%16)/4 (+4 for the second read), v columns 32vb + 16(g%2) + 4(lane%4)
+  f32x16 acc[2][RB];
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[vb][rb][x] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kOpJ / 16; ++ks) {
+    bf16x8 zh[RB], zl[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) split_hilo(zr[rb][ks][0], zr[rb][ks][1], valid[rb], zh[rb], zl[rb]);
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb) {
+      const int jr = 16 * ks + 8 * (g >> 1) + (ii >> 2), ccol = 32 * vb + 16 * (g & 1) + 4 * (ii & 3);
+      const lds_u8* p0 = lw + jr * kOpRowB + 16 * op_chunk(jr, ccol >> 3) + 2 * (ccol & 7);
+      const lds_u8* p1 = lw + (jr + 4) * kOpRowB + 16 * op_chunk(jr + 4, ccol >> 3) + 2 * (ccol & 7);
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+      const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zh[rb], acc[vb][rb], 0, 0, 0);
+        acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zl[rb], acc[vb][rb], 0, 0, 0);
+      }
+    }
+  }
+
+  // partial sums into this wave's LDS (its W slice is no longer read), then wave w finishes
+  // accumulator w (vb = w % 2, rb = w / 2) from all four waves
+  typedef __attribute__((address_space(3))) f32x4 lds_f4;
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(lds_f4*)(lw + ((2 * rb + vb) * 4 + q) * 1024 + 16 * lane) =
+            f32x4{acc[vb][rb][4 * q], acc[vb][rb][4 * q + 1], acc[vb][rb][4 * q + 2], acc[vb][rb][4 * q + 3]};
   __syncthreads();
-  const int rbA = kOpRows * rs + 32 * (wave >> 1);
-  if (rbA >= R) return;  // no barrier follows
-  if (rbA + 64 < R)
-    out_proj_rows<true>(lw, H, R, h, v0, wave & 1, rbA, z, out);
-  else
-    out_proj_rows<false>(lw, H, R, h, v0, wave & 1, rbA, z, out);
+  if (wave >= 2 * RB) return;
+  const int vb = wave & 1, rb = wave >> 1;
+  const int r = r0 + 32 * rb + (lane & 31);
+  if (r >= R) return;
+  float* o = out + (size_t(r) * H + h) * kDv + v0 + 32 * vb + 4 * hi;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum += *(const lds_f4*)((lds_u8*)smem + w * kOpWaveB + (wave * 4 + q) * 1024 + 16 * lane);
+    // D layout: lane holds row lane%32, v = 8q + 4hi + 0..3 of the 32-column block
+    *reinterpret_cast<f32x4*>(o + 8 * q) = sum;
+  }
+}
+
+// Large row counts (prefill chunks): one workgroup per (head, 64 value columns) streams every row
+// slice of 32 through a W_UV slice staged once.  Each wave owns 128 of the 512 j (its W rows in
+// its own LDS) and keeps the z pieces of the next slice in flight while it multiplies the current
+// one; the four partial sums of a slice meet in one of two LDS buffers and waves 0 and 1 finish
+// the two 32-column halves.  z is read once per column half, the second time from the XCD's L2.
+constexpr int kOpPartB = 4 * 2 * 16 * 64 * 4;  // partial sums of one slice: 4 waves x 8 KiB
+
+__global__ __launch_bounds__(256) void out_proj_stream_kernel(int H, int R, const float* __restrict__ z,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kOpWaveB + 2 * kOpPartB];  // 128 KiB
+  constexpr int kHalves = kDv / kOpCols;
+  int h, inner;
+  if (!xcd_head_map(kHalves, H, h, inner)) return;
+  const int v0 = kOpCols * inner;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
+  const int j0 = kOpJ * wave;
+  lds_u8* const lw = (lds_u8*)smem + wave * kOpWaveB;
+  lds_u8* const lpart = (lds_u8*)smem + 4 * kOpWaveB;
+  typedef __attribute__((address_space(3))) f32x4 lds_f4;
+
+  constexpr int kPer = kOpJ * 8 / 64;
+  u32x4 wv[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k, j = c >> 3, ch = c & 7;
+    wv[k] = *reinterpret_cast<const u32x4*>(w_uv + (size_t(h) * kDc + j0 + j) * kDv + v0 + 8 * ch);
+  }
+  const int slices = (R + 31) / 32;
+  auto load_z = [&](f32x4 (&zr)[kOpJ / 16][2], int s) {
+    const int r = 32 * s + (lane & 31);
+    const float* zp = z + (size_t(r < R ? r : 0) * H + h) * kDc + j0 + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < kOpJ / 16; ++ks) {
+      zr[ks][0] = *reinterpret_cast<const f32x4*>(zp + 16 * ks);
+      zr[ks][1] = *reinterpret_cast<const f32x4*>(zp + 16 * ks + 4);
+    }
+  };
+  f32x4 za[kOpJ / 16][2], zb[kOpJ / 16][2];
+  load_z(za, 0);
+  // wait for the first slice here, together with the W_UV slice (an empty asm that reads the
+  // values), rather than letting the compiler move these loads behind the LDS staging
+#pragma unroll
+  for (int ks = 0; ks < kOpJ / 16; ++ks) asm volatile("" : "+v"(za[ks][0]), "+v"(za[ks][1]));
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k, j = c >> 3, ch = c & 7;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lw + j * kOpRowB + 16 * op_chunk(j, ch)) = wv[k];
+  }
+
+  // one slice: multiply the z pieces in `zc` (slice s) while those of slice s+1 load into `zn`.
+  // The loads are unconditional (past the end they repeat the last slice) so that the in-order
+  // wait counts only ever wait for the slice being multiplied.  `buf` alternates the partial-sum
+  // buffers.
+  auto slice = [&](f32x4 (&zc)[kOpJ / 16][2], f32x4 (&zn)[kOpJ / 16][2], int s, int buf) {
+    load_z(zn, min(s + 1, slices - 1));
+    __builtin_amdgcn_sched_barrier(0);  // issue them before the multiplications, not after
+    const bool valid = 32 * s + (lane & 31) < R;
+    f32x16 acc[2];
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[vb][x] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kOpJ / 16; ++ks) {
+      bf16x8 zh, zl;
+      split_hilo(zc[ks][0], zc[ks][1], valid, zh, zl);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) {
+        const int jr = 16 * ks + 8 * (g >> 1) + (ii >> 2), ccol = 32 * vb + 16 * (g & 1) + 4 * (ii & 3);
+        const lds_u8* p0 = lw + jr * kOpRowB + 16 * op_chunk(jr, ccol >> 3) + 2 * (ccol & 7);
+        const lds_u8* p1 = lw + (jr + 4) * kOpRowB + 16 * op_chunk(jr + 4, ccol >> 3) + 2 * (ccol & 7);
+        const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+        const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+        const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zh, acc[vb], 0, 0, 0);
+        acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zl, acc[vb], 0, 0, 0);
+      }
+    }
+    lds_u8* const part = lpart + buf * kOpPartB;
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(lds_f4*)(part + ((wave * 2 + vb) * 4 + q) * 1024 + 16 * lane) =
+            f32x4{acc[vb][4 * q], acc[vb][4 * q + 1], acc[vb][4 * q + 2], acc[vb][4 * q + 3]};
+    // every partial of this slice written; the other buffer, used by the slice before, fully read
+    __syncthreads();
+    if (wave < 2) {
+      const int r = 32 * s + (lane & 31);
+      if (r < R) {
+        float* o = out + (size_t(r) * H + h) * kDv + v0 + 32 * wave + 4 * hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) sum += *(const lds_f4*)(part + ((w * 2 + wave) * 4 + q) * 1024 + 16 * lane);
+          *reinterpret_cast<f32x4*>(o + 8 * q) = sum;
+        }
+      }
+    }
+  };
+  // slices in pairs; an odd count repeats the last slice, which stores the same rows again
+  for (int s = 0; s < slices; s += 2) {
+    slice(za, zb, s, 0);
+    slice(zb, za, min(s + 1, slices - 1), 1);
+  }
 }
 
 }  // namespace
@@ -289,19 +444,29 @@ hipError_t launch_absorb_mfma(const Dims& d, const void* q_c, const void* q_r, c
   const float qscale = d.sm_scale * kLog2e;
   const uint16_t *qc = static_cast<const uint16_t*>(q_c), *qr = static_cast<const uint16_t*>(q_r);
   const uint16_t* wk = static_cast<const uint16_t*>(w_uk);
+  RopeFreq inv{};
+  for (int i = 0; i < d.dr / 2; ++i) inv.v[i] = pow(double(d.rope_base), -2.0 * i / d.dr);
   if (rows <= 4 * 32)  // small batch: 32-row workgroups
     absorb_mfma_kernel<1><<<dim3(xcd_grid((rows + 31) / 32, d.H)), 256, 0, s>>>(
-        d.H, rows, d.dr, d.rope_base, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
+        d.H, rows, d.dr, inv, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
   else
     absorb_mfma_kernel<2><<<dim3(xcd_grid((rows + 63) / 64, d.H)), 256, 0, s>>>(
-        d.H, rows, d.dr, d.rope_base, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
+        d.H, rows, d.dr, inv, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
   return hipGetLastError();
 }
 
 hipError_t launch_out_proj_mfma(const Dims& d, const float* z, const void* w_uv, int rows, float* out,
                                 hipStream_t s) {
-  out_proj_mfma_kernel<<<dim3(xcd_grid((kDv / kOpCols) * ((rows + kOpRows - 1) / kOpRows), d.H)), 256, 0, s>>>(
-      d.H, rows, z, static_cast<const uint16_t*>(w_uv), out);
+  constexpr int kHalves = kDv / kOpCols;
+  if (rows <= 4 * 32)  // small batch: 32-row workgroups, so that a decode step fills the chip
+    out_proj_mfma_kernel<1><<<dim3(xcd_grid(kHalves * ((rows + 31) / 32), d.H)), 256, 0, s>>>(
+        d.H, rows, z, static_cast<const uint16_t*>(w_uv), out);
+  else if (rows <= 8 * 32)
+    out_proj_mfma_kernel<2><<<dim3(xcd_grid(kHalves * ((rows + 63) / 64), d.H)), 256, 0, s>>>(
+        d.H, rows, z, static_cast<const uint16_t*>(w_uv), out);
+  else  // prefill chunks: one streaming workgroup per (head, column half)
+    out_proj_stream_kernel<<<dim3(xcd_grid(kHalves, d.H)), 256, 0, s>>>(d.H, rows, z,
+                                                                        static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
 }
 
