@@ -136,6 +136,61 @@ def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
                       f"NumPy; algorithmic absorbed flops counted) in {el:.1f} s"}
 
 
+def bench_prefill_unabsorbed(args, w) -> dict:
+    """Chunked prefill the unabsorbed way: mla_decompress_kv -> mla_prefill_unabsorbed per step.
+    Same inputs and outputs as bench_prefill; its own algorithmic flops (decompression of every
+    cached latent per head, then 2 * (d_k + d_r) + 2 * d_v per visible pair)."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    inp = gen.make_prefill_inputs(w)
+    dev = torch.device("cuda:0")
+    st = runner.PrefillUnabsorbedStep(inp, dev)
+    if not st.supported():
+        raise SystemExit(f"the unabsorbed prefill does not support workload {w.name}")
+    pairs = int(sum(min(int(inp["lens"][b]), int(inp["q_start"][b]) + i + 1)
+                    for b in range(w.batch) for i in range(w.q_len)))
+    flops_attn = pairs * w.n_heads * (2 * (w.d_k + w.d_r) + 2 * w.d_v)
+    flops_dec = int(np.sum(inp["lens"])) * w.n_heads * 2 * w.d_c * (w.d_k + w.d_v)
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        st.decompress()
+        ev[i][0].record(stream)
+        st.attend()
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    ms_attn = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tf_attn = flops_attn / (ms_attn * 1e-3) / 1e12
+    return {
+        "metric": "MLA chunked-prefill TFLOP/s, unabsorbed path (V3 shape, 1 GPU)",
+        "value": round((flops_attn + flops_dec) / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prior_tokens": w.ctx, "chunk": w.q_len,
+                   "heads": w.n_heads, "d_c": w.d_c, "d_r": w.d_r, "causal_pairs": pairs, "seed": w.seed,
+                   "path": "unabsorbed (decompress + attend)"},
+        "query_tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "kernel": "mla_prefill_unabsorbed", "achieved": round(tf_attn, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf_attn / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(ms_attn, 6), "algorithmic_flops_per_launch": flops_attn},
+        "decompress": {"ms_per_launch": round(ms_step - ms_attn, 6), "algorithmic_flops_per_launch": flops_dec,
+                       "tflops": round(flops_dec / ((ms_step - ms_attn) * 1e-3) / 1e12, 3)},
+    }
+
+
 def bench_prefill(args, w) -> dict:
     """Chunked prefill: absorb -> mla_prefill_chunk -> out_proj per step; MFMA-bound."""
     import numpy as np
@@ -324,6 +379,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/decode_traffic_<workload>.json from two rocprofv3 --pmc runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unabsorbed", action="store_true",
+                    help="prefill workloads: time the unabsorbed path (decompress + attend) instead")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -347,7 +404,7 @@ def main() -> int:
 
     w = gen.WORKLOADS[args.workload]
     if w.kind == "prefill":
-        print(json.dumps(bench_prefill(args, w)), flush=True)
+        print(json.dumps(bench_prefill_unabsorbed(args, w) if args.unabsorbed else bench_prefill(args, w)), flush=True)
         return 0
     if w.kind == "kv_append":
         print(json.dumps(bench_kv_append(args, w)), flush=True)

@@ -183,6 +183,39 @@ mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, 
 mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t q_len,
                              const int32_t* q_start, float* z, float* lse, void* stream);
 
+/* Unabsorbed chunked prefill (row N4), the other path for a chunk of new queries: for long chunks
+ * the per-pair work of plain attention (2 * (d_k + d_r) + 2 * d_v flops) is far below the absorbed
+ * path's (2 * (d_c + d_r) + 2 * d_c), once every cached latent is decompressed per head
+ * ([molayo] formal definition and chunked-prefill note; [ase] Fig. 3 and Fig. 4 left-hand sides).
+ * Only the DeepSeek-V3 shape in bf16 (H 128, d_c 512, d_r 64, d_k = d_v 128) is implemented;
+ * other dims give MLA_ERR_UNSUPPORTED (the absorbed mla_prefill_chunk handles every shape).
+ *
+ * Step 1, decompression: for t < seq_lens[b],
+ *   k[b,h,t,:] = c_t . W_UK[h],  v[b,h,t,:] = c_t . W_UV[h],  k_r[b,t,:] = k^R_t (copied)
+ *   w_uk, w_uv  device bf16 [H, d_c, d_k] / [H, d_c, d_v]
+ *   k, v        device bf16 [batch, H, max_len, d_k] / [.., d_v]   (outputs; rows t >= seq_lens[b]
+ *                                                                  are not written)
+ *   k_r         device bf16 [batch, max_len, d_r]                  (output)
+ *   max_len     host bound >= every seq_lens[b]                                                  */
+mla_status mla_decompress_kv(const mla_dims* dims, const mla_cache* cache, int32_t max_len, const void* w_uk,
+                             const void* w_uv, void* k, void* v, void* k_r, void* stream);
+
+/* Step 2, causal attention over the decompressed keys and values: query i of sequence b sits at
+ * absolute position p = q_start[b] + i and reads keys t <= p, t < seq_lens[b]:
+ *   s_t = (q_c[b,i,h,:] . k[b,h,t,:] + RoPE_p(q_r[b,i,h,:]) . k_r[b,t,:]) * sm_scale
+ *   out[b,i,h,:] = sum_t softmax_t(s) v[b,h,t,:];  lse[b,i,h] = ln sum_t exp(s_t)
+ * This is the output of mla_prefill_chunk followed by mla_out_proj, up to rounding (the
+ * associativity behind absorption).  No visible key gives out = 0, lse = -inf.
+ *   q_c, q_r  device bf16 [batch, q_len, H, d_k] / [.., d_r]  (q_r unrotated)
+ *   q_start   device int32 [batch]
+ *   k, v, k_r as written by mla_decompress_kv with the same max_len
+ *   out       device float [batch, q_len, H, d_v];  lse device float [batch, q_len, H] or NULL   */
+mla_status mla_prefill_unabsorbed(const mla_dims* dims, const mla_cache* cache, int32_t max_len, const void* q_c,
+                                  const void* q_r, const int32_t* q_start, int32_t q_len, const void* k,
+                                  const void* v, const void* k_r, float* out, float* lse, void* stream);
+/* Nonzero when the unabsorbed prefill supports these dims. */
+int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims);
+
 /* Query side of one layer ([ase] "현재 토큰의 Query 만들기", Fig. 1; [molayo] query compression):
  *   c^Q = h . W_DQ;  q_c[r,h,:] = c^Q . W_UQ[h];  q_r[r,h,:] = c^Q . W_QR[h]  (unrotated)
  *   h    device dtype [rows, d_model];  w_dq dtype [d_model, d_cq]

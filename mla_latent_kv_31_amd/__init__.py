@@ -34,11 +34,14 @@ from ._lib import (  # noqa: F401
     mla_decode_partial,
     mla_decode_partial_balanced,
     mla_decode_uses_mfma,
+    mla_decompress_kv,
     mla_kv_append,
     mla_kv_append_workspace_bytes,
     mla_out_proj,
     mla_prefill_chunk,
     mla_prefill_uses_mfma,
+    mla_prefill_unabsorbed,
+    mla_prefill_unabsorbed_supported,
     mla_project_query,
     mla_status_str,
 )

@@ -69,6 +69,9 @@ _SIGNATURES = {
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "mla_decompress_kv": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "mla_prefill_unabsorbed": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "mla_prefill_unabsorbed_supported": (_I32, [_PD]),
     "mla_kv_append_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
     "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
 }
@@ -202,6 +205,22 @@ def mla_project_query(d: MlaDims, d_model: int, d_cq: int, h, w_dq, w_uq, w_qr, 
     _check(library().mla_project_query(ctypes.byref(d), d_model, d_cq, _addr(h), _addr(w_dq), _addr(w_uq),
                                        _addr(w_qr), rows, _addr(q_c), _addr(q_r), _stream(stream)),
            "mla_project_query")
+
+
+def mla_decompress_kv(d: MlaDims, c: MlaCache, max_len: int, w_uk, w_uv, k, v, k_r, stream=None) -> None:
+    _check(library().mla_decompress_kv(ctypes.byref(d), ctypes.byref(c), max_len, _addr(w_uk), _addr(w_uv),
+                                       _addr(k), _addr(v), _addr(k_r), _stream(stream)), "mla_decompress_kv")
+
+
+def mla_prefill_unabsorbed(d: MlaDims, c: MlaCache, max_len: int, q_c, q_r, q_start, q_len: int, k, v, k_r, out,
+                           lse=None, stream=None) -> None:
+    _check(library().mla_prefill_unabsorbed(ctypes.byref(d), ctypes.byref(c), max_len, _addr(q_c), _addr(q_r),
+                                            _addr(q_start), q_len, _addr(k), _addr(v), _addr(k_r), _addr(out),
+                                            _addr(lse), _stream(stream)), "mla_prefill_unabsorbed")
+
+
+def mla_prefill_unabsorbed_supported(d: MlaDims) -> bool:
+    return bool(library().mla_prefill_unabsorbed_supported(ctypes.byref(d)))
 
 
 def mla_kv_append_workspace_bytes(d: MlaDims, d_model: int, rows: int) -> int:

@@ -254,6 +254,52 @@ mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq
   return hip_status(launch_project_query(d, d_model, d_cq, h, w_dq, w_uq, w_qr, rows, q_c, q_r, (hipStream_t)stream));
 }
 
+int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims) {
+  Dims d;
+  return check_dims(dims, &d) == MLA_OK && prefill_unabsorbed_supported(d) ? 1 : 0;
+}
+
+mla_status mla_decompress_kv(const mla_dims* dims, const mla_cache* cache, int32_t max_len, const void* w_uk,
+                             const void* w_uv, void* k, void* v, void* k_r, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  if (!prefill_unabsorbed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (max_len < 1) return MLA_ERR_SHAPE;
+  if (int64_t(c.batch) * d.H * int64_t(max_len) * d.dk > (int64_t(1) << 40)) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(w_uk));
+  MLA_TRY(ptr_ok(w_uv));
+  MLA_TRY(ptr_ok(k));
+  MLA_TRY(ptr_ok(v));
+  MLA_TRY(ptr_ok(k_r));
+  if (c.batch == 0) return MLA_OK;
+  return hip_status(launch_decompress_kv(d, c, max_len, w_uk, w_uv, k, v, k_r, (hipStream_t)stream));
+}
+
+mla_status mla_prefill_unabsorbed(const mla_dims* dims, const mla_cache* cache, int32_t max_len, const void* q_c,
+                                  const void* q_r, const int32_t* q_start, int32_t q_len, const void* k,
+                                  const void* v, const void* k_r, float* out, float* lse, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  if (!prefill_unabsorbed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (max_len < 1 || q_len < 0) return MLA_ERR_SHAPE;
+  if (int64_t(c.batch) * d.H * int64_t(max_len) * d.dk > (int64_t(1) << 40)) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(q_c));
+  MLA_TRY(ptr_ok(q_r));
+  MLA_TRY(ptr_ok(q_start));
+  MLA_TRY(ptr_ok(k));
+  MLA_TRY(ptr_ok(v));
+  MLA_TRY(ptr_ok(k_r));
+  MLA_TRY(ptr_ok(out));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (c.batch == 0 || q_len == 0) return MLA_OK;
+  return hip_status(launch_attend_unabsorbed(d, c, max_len, q_c, q_r, q_start, q_len, k, v, k_r, out, lse,
+                                             (hipStream_t)stream));
+}
+
 static bool kv_append_uses_mfma(const mla_dims* dims, const Dims& d, int32_t d_model) {
   return !(dims->flags & MLA_FLAG_FORCE_GENERIC) && kv_append_mfma_supported(d, d_model);
 }

@@ -69,6 +69,14 @@ hipError_t launch_out_proj_generic(const Dims& d, const float* z, const void* w_
 hipError_t launch_project_query(const Dims& d, int d_model, int d_cq, const void* h, const void* w_dq,
                                 const void* w_uq, const void* w_qr, int rows, void* q_c, void* q_r,
                                 hipStream_t s);
+// ---- unabsorbed chunked prefill for the DeepSeek-V3 shape (bf16, 128 heads, 512 / 64 / 128)
+bool prefill_unabsorbed_supported(const Dims& d);
+hipError_t launch_decompress_kv(const Dims& d, const Cache& c, int max_len, const void* w_uk, const void* w_uv,
+                                void* k_out, void* v_out, void* kr_out, hipStream_t s);
+hipError_t launch_attend_unabsorbed(const Dims& d, const Cache& c, int max_len, const void* q_c, const void* q_r,
+                                    const int32_t* q_start, int q_len, const void* k, const void* v, const void* kr,
+                                    float* out, float* lse, hipStream_t s);
+
 // ---- bf16 MFMA cache write for the DeepSeek-V3 latent shape (d_c 512, d_r 64, d_model % 256 == 0)
 bool kv_append_mfma_supported(const Dims& d, int d_model);
 size_t kv_append_mfma_workspace(int d_model, int rows);

@@ -168,3 +168,47 @@ class PrefillStep:
         self.absorb(stream)
         self.attend(stream)
         self.out_proj(stream)
+
+
+class PrefillUnabsorbedStep:
+    """Device buffers of one unabsorbed chunked-prefill call; ``run()`` enqueues the per-head
+    decompression of the cached latents, then causal attention over the decompressed keys and
+    values (output in the value space, like PrefillStep.out)."""
+
+    def __init__(self, inp: dict, device="cuda:0", max_len: int | None = None):
+        w = inp["workload"]
+        self.w = w
+        self.device = torch.device(device)
+        self.d = dims_for(w)
+        dev = self.device
+        self.q_c = to_device(inp["q_c"], dev)
+        self.q_r = to_device(inp["q_r"], dev)
+        self.w_uk = to_device(inp["w_uk"], dev)
+        self.w_uv = to_device(inp["w_uv"], dev)
+        self.pool = to_device(inp["pool"], dev)
+        self.page_table = to_device(inp["page_table"], dev)
+        self.lens = to_device(inp["lens"].astype(np.int32), dev)
+        self.q_start = to_device(inp["q_start"].astype(np.int32), dev)
+        self.B, self.Sq = int(inp["q_c"].shape[0]), int(inp["q_c"].shape[1])
+        self.max_len = int(max_len or max(1, int(np.max(inp["lens"]))))
+        H = w.n_heads
+        self.k = torch.empty((self.B, H, self.max_len, w.d_k), dtype=torch.bfloat16, device=dev)
+        self.v = torch.empty((self.B, H, self.max_len, w.d_v), dtype=torch.bfloat16, device=dev)
+        self.k_r = torch.empty((self.B, self.max_len, w.d_r), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
+        self.c = L.cache(self.pool, self.page_table, self.lens)
+
+    def supported(self) -> bool:
+        return L.mla_prefill_unabsorbed_supported(self.d)
+
+    def decompress(self, stream=None):
+        L.mla_decompress_kv(self.d, self.c, self.max_len, self.w_uk, self.w_uv, self.k, self.v, self.k_r, stream)
+
+    def attend(self, stream=None):
+        L.mla_prefill_unabsorbed(self.d, self.c, self.max_len, self.q_c, self.q_r, self.q_start, self.Sq, self.k,
+                                 self.v, self.k_r, self.out, self.lse, stream)
+
+    def run(self, stream=None):
+        self.decompress(stream)
+        self.attend(stream)
