@@ -11,12 +11,14 @@
 // decompress_kv_kernel: per (128 tokens of a sequence, head), out^T = W^T . C^T for the head's
 // W_UK and W_UV (256 output columns, K = 512) with v_mfma_f32_32x32x16_bf16.  The latent rows come
 // through the page table straight from the pool as the B operand (16 bytes per lane); the weight
-// slice is staged in LDS 32 rows at a time (double-buffered) and read with ds_read_b64_tr_b16.
+// slice streams into LDS 32 rows at a time through direct global-to-LDS transfers, three chunks in
+// flight, and is read with ds_read_b64_tr_b16.
 // Results go through LDS and out as whole 256-byte rows of K and V ([b][h][t][128] bf16); the
 // head-0 workgroups also copy the rotary keys to kr ([b][t][64] bf16).
 //
 // attend_unabsorbed_kernel: per (128 queries, head, sequence), four waves of 32 queries.  Keys and
-// values stream through LDS in 32-token tiles (double-buffered, staged through registers).  Scores
+// values stream into LDS in 32-token tiles through direct global-to-LDS transfers, three tiles in
+// flight.  Scores
 // are computed transposed, S^T = [K | k^R] . Q^T (tokens on M, queries on N, 12 k-steps), so every
 // lane holds 16 scores of one query and the softmax stays in the lane plus one v_permlane32_swap.
 // Online softmax with a running maximum; the accumulator is rescaled only when a maximum moved.
@@ -51,24 +53,42 @@ __device__ __forceinline__ bf16x8 tr_pair(const lds_u8* p0, const lds_u8* p1) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// One 16-byte-per-lane transfer from global memory straight into LDS at M0 + 16 * lane, waited for
+// with explicit vmcnt waits (the compiler does not see that it writes LDS).
+__device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const void* gbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase) : "memory");
+}
+// The same with a full 64-bit address per lane (for rows anywhere in a cache pool of any size).
+__device__ __forceinline__ void dma16_at(uint32_t lds_dst, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_dst), "v"(src) : "memory");
+}
+
 // ------------------------------------------------------------------------------- decompression
-constexpr int kDcTok = 128;                  // tokens per workgroup (4 waves x 32)
-constexpr int kDcJ = 32;                     // weight rows staged per chunk
-constexpr int kDcRowB = 2 * kRowB;           // a staged weight row: 128 W_UK + 128 W_UV columns
-constexpr int kDcChunkB = kDcJ * kDcRowB;    // 16 KiB
-constexpr int kDcOutRow = 2 * kRowB + 16;     // staged output row (K | V) + padding against bank conflicts
-constexpr int kDcOutB = kDcTok * kDcOutRow;    // 66 KiB output staging
+constexpr int kDcTok = 128;                    // tokens per workgroup (4 waves x 32)
+constexpr int kDcJ = 32;                       // weight rows per chunk
+constexpr int kDcChunks = kDc / kDcJ;          // 16
+constexpr int kDcWB = 2 * kDcJ * kRowB;        // 16 KiB: 32 W_UK rows | 32 W_UV rows
+constexpr int kDcCB = kDcTok * kDcJ * 2;        // 8 KiB: the 128 tokens' latents over the chunk's 32 j
+constexpr int kDcChunkB = kDcWB + kDcCB;        // 24 KiB
+constexpr int kDcBuf = 3;                       // chunk buffers: one in use, two in flight
+constexpr int kDcXfer = kDcChunkB / 1024 / 4;   // 6 one-KiB transfers per wave per chunk
+constexpr int kDcOutRow = 2 * kRowB + 16;      // staged output row (K | V) + padding against bank conflicts
+constexpr int kDcOutB = kDcTok * kDcOutRow;    // 66 KiB output staging (reuses the chunk buffers)
+constexpr int kDcLds = kDcOutB > kDcBuf * kDcChunkB ? kDcOutB : kDcBuf * kDcChunkB;
 
-// 16-byte chunk c (0..31) of staged weight row r sits at c ^ 4*(r & 3): the transposing reads of
-// 4 rows x 4 chunks by 32 lanes then cover 16 distinct bank groups.
-__device__ __forceinline__ int dc_swz(int r, int c) { return c ^ ((r & 3) << 2); }
+// 256-byte rows (K, V, staged weights): 16-byte chunk c of row r at c ^ f(r),
+// f(r) = ((r & 3) << 2) | ((r >> 2) & 3): 16 consecutive rows at one logical chunk (row-wise reads)
+// and 4 rows x 4 chunks (transposing reads) hit 16 distinct bank groups.  128-byte k^R rows: chunk
+// c of row r at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int kr_swz(int r) { return (r >> 1) & 7; }
 
-__global__ __launch_bounds__(256) void decompress_kv_kernel(Cache c, int max_len, const uint16_t* __restrict__ w_uk,
-                                                            const uint16_t* __restrict__ w_uv,
-                                                            uint16_t* __restrict__ k_out,
-                                                            uint16_t* __restrict__ v_out,
-                                                            uint16_t* __restrict__ kr_out) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kDcOutB];  // 2 weight chunks, then the output
+__global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_len, const uint16_t* __restrict__ w_uk,
+                                                               const uint16_t* __restrict__ w_uv,
+                                                               uint16_t* __restrict__ k_out,
+                                                               uint16_t* __restrict__ v_out,
+                                                               uint16_t* __restrict__ kr_out) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kDcLds];
   lds_u8* const lbase = (lds_u8*)smem;
   const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int len = min(c.seq_lens[b], c.max_pages * c.page_size);
@@ -77,37 +97,48 @@ __global__ __launch_bounds__(256) void decompress_kv_kernel(Cache c, int max_len
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
   const uint16_t* pool = static_cast<const uint16_t*>(c.pool);
 
-  // B operand: latent row of token t0 + 32*wave + lane%32 (clamped inside the sequence)
-  const int tok = min(t0 + 32 * wave + (lane & 31), len - 1);
-  const uint16_t* crow = pool + row_index(c.page_table, c.max_pages, c.page_size, b, tok) * kW + 8 * hi;
-
-  // staging: chunk k covers weight rows j = 32k .. 32k+31; thread t moves 16-byte pieces
-  // p = t + 256x (x < 4): row p / 32, piece p % 32 (pieces 0..15 from W_UK, 16..31 from W_UV)
-  u32x4 st[4];
-  auto load_w = [&](int k) {
+  // chunk transfers of 1 KiB, six per wave.  Weight transfers T = 4*wave + x (x < 4): T < 8 W_UK
+  // rows 32k + 4T .., else W_UV rows 32k + 4(T-8) .. (256 B each, lane L fills LDS chunk L%16 of
+  // row L/16).  Latent transfers u = 2*wave + (x-4) (x = 4, 5): tokens 16u .. 16u+15 over
+  // j = 32k .. 32k+31 (64 B per token, lane L fills chunk L%4 of token row L/4), so a wave fetches
+  // the latents of its own 32 tokens.  Latent rows come through the page table (clamped inside the
+  // sequence); each lane keeps the pool offsets of its two token rows.
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lbase));
+  const uint16_t* const ukh = w_uk + size_t(h) * kDc * kDk;
+  const uint16_t* const uvh = w_uv + size_t(h) * kDc * kDk;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t* crow[2];  // the token rows of this lane's latent transfers, at its chunk
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * (2 * wv + u) + (lane >> 2), cc = (lane & 3) ^ ((r >> 2) & 3);
+    crow[u] = pool + row_index(c.page_table, c.max_pages, c.page_size, b, min(t0 + r, len - 1)) * kW + 8 * cc;
+  }
+  auto dma_chunk = [&](int k, int buf) {
+    const uint32_t dst = lds0 + uint32_t(buf * kDcChunkB);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int p = threadIdx.x + 256 * x, r = p >> 5, q = p & 31;
-      const uint16_t* src = (q < 16 ? w_uk : w_uv) + (size_t(h) * kDc + 32 * k + r) * kDk + 8 * (q & 15);
-      st[x] = *reinterpret_cast<const u32x4*>(src);
+      const int T = 4 * wv + x;
+      const int r = 4 * (T & 7) + (lane >> 4), cc = (lane & 15) ^ kv_swz(r);
+      dma16(dst + uint32_t(T * 1024), uint32_t((kDcJ * k + r) * kRowB + 16 * cc), T < 8 ? ukh : uvh);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16_at(dst + uint32_t(kDcWB + (2 * wv + u) * 1024), crow[u] + kDcJ * k);
   };
-  auto store_w = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int p = threadIdx.x + 256 * x, r = p >> 5, q = p & 31;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + buf * kDcChunkB + r * kDcRowB +
-                                                                  16 * dc_swz(r, q)) = st[x];
-    }
+  // B operand: latents of token 32*wave + lane%32 at j = 16s + 8hi of the chunk (64-byte token rows,
+  // chunk c of row r at c ^ ((r >> 2) & 3))
+  auto b_op = [&](int buf, int s) {
+    const int r = 32 * wave + (lane & 31);
+    return lds16(lbase + buf * kDcChunkB + kDcWB + r * 64 + 16 * ((2 * s + hi) ^ ((r >> 2) & 3)));
   };
   // A operand of output block ob (0..3: K columns 32ob.., 4..7: V) at k-step s of a chunk: group g
-  // addresses rows 8*(g/2) + (lane%16)/4 (+4 for the second read), columns 32ob + 16(g%2) + 4(lane%4)
+  // addresses rows 16s + 8(g/2) + (lane%16)/4 (+4 for the second read), columns 32(ob%4) + 16(g%2)
+  // + 4(lane%4) of the K or V half
   auto a_op = [&](int buf, int s, int ob) {
     const int r = 16 * s + 8 * (g >> 1) + (ii >> 2);
-    const int col = 32 * ob + 16 * (g & 1) + 4 * (ii & 3);
-    const lds_u8* base = lbase + buf * kDcChunkB;
-    const lds_u8* p0 = base + r * kDcRowB + 16 * dc_swz(r, col >> 3) + 2 * (col & 7);
-    const lds_u8* p1 = base + (r + 4) * kDcRowB + 16 * dc_swz(r + 4, col >> 3) + 2 * (col & 7);
+    const int col = 32 * (ob & 3) + 16 * (g & 1) + 4 * (ii & 3);
+    const lds_u8* base = lbase + buf * kDcChunkB + (ob >> 2) * (kDcJ * kRowB);  // K or V half
+    const lds_u8* p0 = base + r * kRowB + 16 * ((col >> 3) ^ kv_swz(r)) + 2 * (col & 7);
+    const lds_u8* p1 = base + (r + 4) * kRowB + 16 * ((col >> 3) ^ kv_swz(r + 4)) + 2 * (col & 7);
     return tr_pair(p0, p1);
   };
 
@@ -117,33 +148,29 @@ __global__ __launch_bounds__(256) void decompress_kv_kernel(Cache c, int max_len
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[ob][x] = 0.f;
 
-  constexpr int kChunks = kDc / kDcJ;  // 16
-  bf16x8 bcur[2], bnxt[2];
+  // chunks k and k+1 in flight while chunk k is multiplied; every iteration issues the same
+  // transfers (past the end they repeat the last chunk into the free buffer), so one wait count
+  // fits all
 #pragma unroll
-  for (int s = 0; s < 2; ++s) bcur[s] = *reinterpret_cast<const bf16x8*>(crow + 16 * s);
-  load_w(0);
-  store_w(0);
-  __syncthreads();
-  for (int k = 0; k < kChunks; ++k) {
-    const int buf = k & 1;
-    const int kn = min(k + 1, kChunks - 1);  // unconditional loads keep the wait counts exact
+  for (int k = 0; k < kDcBuf - 1; ++k) dma_chunk(k, k);
+  for (int k = 0; k < kDcChunks; ++k) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDcXfer) : "memory");  // chunk k landed (own part)
+    __syncthreads();  // every wave's part landed; the buffer of chunk k-1 is free
+    dma_chunk(min(k + kDcBuf - 1, kDcChunks - 1), (k + kDcBuf - 1) % kDcBuf);
+    const int buf = k % kDcBuf;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) bnxt[s] = *reinterpret_cast<const bf16x8*>(crow + 32 * kn + 16 * s);
-    load_w(kn);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 bq = b_op(buf, s);
 #pragma unroll
       for (int ob = 0; ob < 8; ++ob)
-        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op(buf, s, ob), bcur[s], acc[ob], 0, 0, 0);
-    if (k + 1 < kChunks) store_w(buf ^ 1);  // that buffer was last read before the previous barrier
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) bcur[s] = bnxt[s];
+        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op(buf, s, ob), bq, acc[ob], 0, 0, 0);
+    }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with the chunk buffers and no transfer is in flight
 
   // D layout: lane holds token lane%32 of the wave and columns 32ob + 8(x/4) + 4hi + x%4.  Stage
-  // [128 tokens][K row | V row] in LDS (the weight chunks are done), then write whole rows.
+  // [128 tokens][K row | V row] in LDS, then write whole rows.
   {
     lds_u8* const orow = lbase + (32 * wave + (lane & 31)) * kDcOutRow;
 #pragma unroll
@@ -182,24 +209,21 @@ constexpr int kAtT = 32;                     // tokens per tile
 constexpr int kTileKB = kAtT * kRowB;        // 8 KiB of K
 constexpr int kTileRB = kAtT * kDr * 2;      // 4 KiB of k^R
 constexpr int kTileB = 2 * kTileKB + kTileRB;  // K | V | k^R: 20 KiB
-constexpr int kAtPieces = kTileB / 16 / 256;   // 5 x 16 B per thread
+constexpr int kAtBuf = 4;                      // LDS tile buffers: one in use, three in flight
+constexpr int kAtXfer = kTileB / 1024 / 4;     // 5 one-KiB transfers per wave per tile
 
-// K and V rows: 16-byte chunk c (0..15) of row r at c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3):
-// 16 consecutive rows at one logical chunk (score reads) and 4 rows x 4 chunks (transposing reads)
-// hit 16 distinct bank groups.  k^R rows (8 chunks, 128 B): chunk c of row r at c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int kr_swz(int r) { return (r >> 1) & 7; }
+// K, V and k^R tile rows use the swizzles of the decompression section above.
 
 struct RopeTab {
   double v[kDr / 2];
 };
 
-__global__ __launch_bounds__(256) void attend_unabsorbed_kernel(
+__global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
     const int32_t* __restrict__ seq_lens, int cap, int max_len, const uint16_t* __restrict__ q_c,
     const uint16_t* __restrict__ q_r, const int32_t* __restrict__ q_start, int q_len, float qscale, RopeTab rope,
     const uint16_t* __restrict__ k_in, const uint16_t* __restrict__ v_in, const uint16_t* __restrict__ kr_in,
     float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileB];  // 40 KiB
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kAtBuf * kTileB];  // 80 KiB
   lds_u8* const lbase = (lds_u8*)smem;
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
@@ -242,46 +266,29 @@ __global__ __launch_bounds__(256) void attend_unabsorbed_kernel(
     }
   }
 
-  // ---- tile staging: thread t moves 16-byte pieces p = t + 256x (x < 5) of the 20 KiB tile
-  // (pieces 0..511 K, 512..1023 V, 1024..1279 k^R), swizzled into LDS
-  const size_t kvbase = (size_t(b) * kH + h) * max_len;
-  u32x4 st[kAtPieces];
-  // rows past the sequence end are loaded from a valid row and replaced by zeros: their buffer
-  // memory may hold anything, and 0 x NaN would reach the weighted sum
-  auto load_tile = [&](int j) {
+  // ---- tile transfers: transfer T = 5*wave + x (x < 5) of a tile moves 1 KiB: T < 8 K rows
+  // 4T..4T+3, T < 16 V rows 4(T-8).., else k^R rows 8(T-16)..+7.  Lane L fills LDS chunk L of the
+  // transfer; the global chunk it reads is the one the swizzle places there.  Rows past the
+  // sequence end copy row len-1 (finite; their scores are masked, so their weight is 0).
+  const uint16_t* const kbase = k_in + (size_t(b) * kH + h) * max_len * kDk;
+  const uint16_t* const vbase = v_in + (size_t(b) * kH + h) * max_len * kDk;
+  const uint16_t* const rbase = kr_in + size_t(b) * max_len * kDr;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lbase));
+  auto dma_tile = [&](int j, int buf) {  // tile j into LDS buffer buf
     const int tt0 = kAtT * j;
+    const uint32_t dst = lds0 + uint32_t(buf * kTileB);
 #pragma unroll
-    for (int x = 0; x < kAtPieces; ++x) {
-      const int p = threadIdx.x + 256 * x;
-      const uint16_t* src;
-      int r;
-      if (p < 1024) {
-        r = (p & 511) >> 4;
-        const int q = p & 15;
-        src = (p < 512 ? k_in : v_in) + (kvbase + min(tt0 + r, len - 1)) * kDk + 8 * q;
+    for (int x = 0; x < kAtXfer; ++x) {
+      const int T = kAtXfer * __builtin_amdgcn_readfirstlane(wave) + x;
+      if (T < 16) {
+        const int r = 4 * (T & 7) + (lane >> 4), c = (lane & 15) ^ kv_swz(r);
+        const uint32_t voff = uint32_t(min(tt0 + r, len - 1) * kRowB + 16 * c);
+        dma16(dst + uint32_t(T * 1024), voff, T < 8 ? kbase : vbase);
       } else {
-        r = (p - 1024) >> 3;
-        const int q = p & 7;
-        src = kr_in + (size_t(b) * max_len + min(tt0 + r, len - 1)) * kDr + 8 * q;
+        const int r = 8 * (T - 16) + (lane >> 3), c = (lane & 7) ^ kr_swz(r);
+        const uint32_t voff = uint32_t(min(tt0 + r, len - 1) * (kDr * 2) + 16 * c);
+        dma16(dst + uint32_t(T * 1024), voff, rbase);
       }
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-      st[x] = tt0 + r < len ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    lds_u8* const tb = lbase + buf * kTileB;
-#pragma unroll
-    for (int x = 0; x < kAtPieces; ++x) {
-      const int p = threadIdx.x + 256 * x;
-      int off;
-      if (p < 1024) {
-        const int r = (p & 511) >> 4, q = p & 15;
-        off = (p < 512 ? 0 : kTileKB) + r * kRowB + 16 * (q ^ kv_swz(r));
-      } else {
-        const int r = (p - 1024) >> 3, q = p & 7;
-        off = 2 * kTileKB + r * (kDr * 2) + 16 * (q ^ kr_swz(r));
-      }
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tb + off) = st[x];
     }
   };
   // score A operand (rows = tokens): row lane%32, logical chunk 2ks + hi
@@ -308,16 +315,19 @@ __global__ __launch_bounds__(256) void attend_unabsorbed_kernel(
   float m_run = -INFINITY, l_lane = 0.f;
   const int wq_last = qs + min(q0 + 32 * wave + 31, q_len - 1);  // the wave's last query position
 
+  // tiles 0..2 in flight before the loop; past the last tile the transfers repeat it (into a
+  // buffer nobody reads), which keeps every wait count uniform
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+#pragma unroll
+    for (int k = 0; k < kAtBuf - 1; ++k) dma_tile(min(k, ntiles - 1), k);
   }
-  __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    load_tile(min(j + 1, ntiles - 1));  // unconditional: exact wait counts
-    __builtin_amdgcn_sched_barrier(0);
-    const lds_u8* const tb = lbase + buf * kTileB;
+    // own transfers of tile j done (tiles j+1, j+2 may fly); the barrier makes every wave's part
+    // visible and frees the buffer of tile j-1 for tile j+3
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kAtXfer) : "memory");
+    __syncthreads();
+    dma_tile(min(j + kAtBuf - 1, ntiles - 1), (j + kAtBuf - 1) % kAtBuf);
+    const lds_u8* const tb = lbase + (j % kAtBuf) * kTileB;
     const int tt0 = kAtT * j;
     if (tt0 <= wq_last) {  // the wave sees some token of this tile (uniform)
       f32x16 s;
@@ -373,9 +383,8 @@ __global__ __launch_bounds__(256) void attend_unabsorbed_kernel(
         for (int db = 0; db < 4; ++db)
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op(tb, sk, db), sk ? pb1 : pb0, acc[db], 0, 0, 0);
     }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);  // that buffer was last read before the previous barrier
-    __syncthreads();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no transfer outlives the workgroup
 
   // ---- normalise and write: lane holds query qi, values 32db + 8(x/4) + 4hi + x%4
   const float l_tot = [&] {
