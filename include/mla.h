@@ -193,10 +193,13 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const
  * Step 1, decompression: for t < seq_lens[b],
  *   k[b,h,t,:] = c_t . W_UK[h],  v[b,h,t,:] = c_t . W_UV[h],  k_r[b,t,:] = k^R_t (copied)
  *   w_uk, w_uv  device bf16 [H, d_c, d_k] / [H, d_c, d_v]
- *   k, v        device bf16 [batch, H, max_len, d_k] / [.., d_v]   (outputs; rows t >= seq_lens[b]
- *                                                                  are not written)
- *   k_r         device bf16 [batch, max_len, d_r]                  (output)
- *   max_len     host bound >= every seq_lens[b]                                                  */
+ *   k, v        device binary16 (fp16) [batch, H, max_len, d_k] / [.., d_v]   (outputs, fp32 sums
+ *               rounded once; rows t >= seq_lens[b] are not written)
+ *   k_r         device binary16 [batch, max_len, d_r]                          (output)
+ *   max_len     host bound >= every seq_lens[b]
+ * The intermediates are binary16 rather than bf16 for three more significand bits at the same
+ * MFMA rate; their magnitudes must stay below 65504 (K and V of RMS-normalised latents are
+ * orders of magnitude below it).                                                               */
 mla_status mla_decompress_kv(const mla_dims* dims, const mla_cache* cache, int32_t max_len, const void* w_uk,
                              const void* w_uv, void* k, void* v, void* k_r, void* stream);
 

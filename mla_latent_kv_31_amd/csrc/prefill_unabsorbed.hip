@@ -1,25 +1,32 @@
-// Unabsorbed chunked prefill on bf16 MFMA (gfx950), DeepSeek-V3 shape (128 heads, d_c 512,
-// d_r 64, d_k = d_v = 128).
+// Unabsorbed chunked prefill on MFMA (gfx950), DeepSeek-V3 shape (128 heads, d_c 512, d_r 64,
+// d_k = d_v = 128).
 //
 // For a chunk of Sq new queries per sequence the absorbed path pays 2 * (576 + 512) flops per
 // (query head, key) pair.  Decompressing every cached latent once per chunk into per-head keys
 // and values ([molayo] formal definition: K_h = C W_UK[h], V_h = C W_UV[h]) costs 2 * 2 * 512 * 128
 // flops per (token, head) and leaves 2 * (192 + 128) per pair: plain multi-head attention with a
 // 192-wide score (content part plus the shared rotary key, [ase] Fig. 2) and a 128-wide value.
-// Both per-head projections of the absorbed path disappear as well.  Two launches:
+// Both per-head projections of the absorbed path disappear as well.
+//
+// Precision: the decompression multiplies the bf16 cache and weights exactly as stored; what it
+// produces (K, V, and the copied k^R) is kept in binary16, which carries three more significand
+// bits than bf16 at the same MFMA rate, and the attention runs on binary16 MFMAs with the query
+// and the probabilities in binary16 too.  Every rounding of the path is then 2^-11 relative
+// instead of 2^-8.  Binary16 holds magnitudes up to 65504; K and V of RMS-normalised latents stay
+// orders of magnitude below that.  Two launches:
 //
 // decompress_kv_kernel: per (128 tokens of a sequence, head), out^T = W^T . C^T for the head's
-// W_UK and W_UV (256 output columns, K = 512) with v_mfma_f32_32x32x16_bf16.  The latent rows come
-// through the page table straight from the pool as the B operand (16 bytes per lane); the weight
-// slice streams into LDS 32 rows at a time through direct global-to-LDS transfers, three chunks in
-// flight, and is read with ds_read_b64_tr_b16.
-// Results go through LDS and out as whole 256-byte rows of K and V ([b][h][t][128] bf16); the
-// head-0 workgroups also copy the rotary keys to kr ([b][t][64] bf16).
+// W_UK and W_UV (256 output columns, K = 512) with v_mfma_f32_32x32x16_bf16.  K is walked in 16
+// chunks of 32: each chunk's 32 W_UK and 32 W_UV rows and the matching 64 bytes of the 128 tokens'
+// latent rows (through the page table) stream into LDS by direct global-to-LDS transfers, two
+// chunks in flight while one is multiplied.  The weights are read with ds_read_b64_tr_b16 as the
+// A operand, the latents row-wise as the B operand.
+// Results go through LDS and out as whole 256-byte rows of K and V ([b][h][t][128] binary16);
+// the head-0 workgroups also copy the rotary keys to kr ([b][t][64] binary16).
 //
 // attend_unabsorbed_kernel: per (128 queries, head, sequence), four waves of 32 queries.  Keys and
 // values stream into LDS in 32-token tiles through direct global-to-LDS transfers, three tiles in
-// flight.  Scores
-// are computed transposed, S^T = [K | k^R] . Q^T (tokens on M, queries on N, 12 k-steps), so every
+// flight.  Scores are computed transposed, S^T = [K | k^R] . Q^T (tokens on M, queries on N, 12 k-steps), so every
 // lane holds 16 scores of one query and the softmax stays in the lane plus one v_permlane32_swap.
 // Online softmax with a running maximum; the accumulator is rescaled only when a maximum moved.
 // The weighted sum is accumulated transposed, O^T += V^T . P^T, with V^T from transposing reads in
@@ -34,6 +41,7 @@ namespace mla {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -52,6 +60,12 @@ __device__ __forceinline__ bf16x8 tr_pair(const lds_u8* p0, const lds_u8* p1) {
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+__device__ __forceinline__ f16x8 lds16h(const lds_u8* p) { return __builtin_bit_cast(f16x8, lds16(p)); }
+__device__ __forceinline__ f16x8 tr_pair_h(const lds_u8* p0, const lds_u8* p1) {
+  return __builtin_bit_cast(f16x8, tr_pair(p0, p1));
+}
+// binary16 bits of a float, round to nearest even
+__device__ __forceinline__ uint32_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
 // One 16-byte-per-lane transfer from global memory straight into LDS at M0 + 16 * lane, waited for
 // with explicit vmcnt waits (the compiler does not see that it writes LDS).
@@ -179,8 +193,8 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
       for (int q = 0; q < 4; ++q) {
         const int col = 32 * ob + 8 * q + 4 * hi;  // 0..255 across K | V
         u32x2 v;
-        v[0] = uint32_t(f32_to_bf16(acc[ob][4 * q])) | (uint32_t(f32_to_bf16(acc[ob][4 * q + 1])) << 16);
-        v[1] = uint32_t(f32_to_bf16(acc[ob][4 * q + 2])) | (uint32_t(f32_to_bf16(acc[ob][4 * q + 3])) << 16);
+        v[0] = f16_bits(acc[ob][4 * q]) | (f16_bits(acc[ob][4 * q + 1]) << 16);
+        v[1] = f16_bits(acc[ob][4 * q + 2]) | (f16_bits(acc[ob][4 * q + 3]) << 16);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(orow + 2 * col) = v;
       }
   }
@@ -193,12 +207,16 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
     uint16_t* dst = (q < 16 ? k_out : v_out) + (obase + t) * kDk + 8 * (q & 15);
     *reinterpret_cast<u32x4*>(dst) = v;
   }
-  if (h == 0) {  // rotary keys of these tokens: 8 pieces of 16 B per token
+  if (h == 0) {  // rotary keys of these tokens, bf16 -> binary16: 8 pieces of 8 values per token
     for (int idx = threadIdx.x; idx < ntok * 8; idx += 256) {
       const int t = idx >> 3, q = idx & 7;
       const uint16_t* src = pool + row_index(c.page_table, c.max_pages, c.page_size, b, t0 + t) * kW + kDc + 8 * q;
-      *reinterpret_cast<u32x4*>(kr_out + (size_t(b) * max_len + t0 + t) * kDr + 8 * q) =
-          *reinterpret_cast<const u32x4*>(src);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+      u32x4 y;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        y[k] = f16_bits(__uint_as_float(x[k] << 16)) | (f16_bits(__uint_as_float(x[k] & 0xffff0000u)) << 16);
+      *reinterpret_cast<u32x4*>(kr_out + (size_t(b) * max_len + t0 + t) * kDr + 8 * q) = y;
     }
   }
 }
@@ -211,6 +229,7 @@ constexpr int kTileRB = kAtT * kDr * 2;      // 4 KiB of k^R
 constexpr int kTileB = 2 * kTileKB + kTileRB;  // K | V | k^R: 20 KiB
 constexpr int kAtBuf = 4;                      // LDS tile buffers: one in use, three in flight
 constexpr int kAtXfer = kTileB / 1024 / 4;     // 5 one-KiB transfers per wave per tile
+constexpr float kPShift = 15.f;                // log2 of the probability scale
 
 // K, V and k^R tile rows use the swizzles of the decompression section above.
 
@@ -238,15 +257,23 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
   const int t_end = min(len, max(qs + min(q0 + kAtQ, q_len), 0));
   const int ntiles = (t_end + kAtT - 1) / kAtT;
 
-  // ---- Q^T operand (B of the score MFMA): query qi, k = 16ks + 8hi .. +7; the content part is
-  // q_c as stored (exact), the rotary part is rotated here at qpos and rounded to bf16 once; the
-  // scale sm_scale*log2(e) is applied to the float scores instead
-  bf16x8 qf[12];
+  // ---- Q^T operand (B of the score MFMA): query qi, k = 16ks + 8hi .. +7, in binary16; the
+  // content part is q_c as stored (bf16 values from 2^-17 to 65504 are binary16 values), the rotary
+  // part is rotated here at qpos and rounded once; the scale sm_scale*log2(e) is applied to the
+  // float scores instead
+  f16x8 qf[12];
   {
     const size_t qrow = (size_t(b) * q_len + min(qi, q_len - 1)) * kH + h;
     const uint16_t* qcp = q_c + qrow * kDk + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qcp + 16 * ks);
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qcp + 16 * ks);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qf[ks][2 * k] = (_Float16)__uint_as_float(x[k] << 16);
+        qf[ks][2 * k + 1] = (_Float16)__uint_as_float(x[k] & 0xffff0000u);
+      }
+    }
     const uint16_t* qrp = q_r + qrow * kDr + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -260,8 +287,8 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
         float sn, cs;
         sincosf(float(rd), &sn, &cs);
         const float x1 = bf16_to_f32(uint16_t(v[k] & 0xffffu)), x2 = bf16_to_f32(uint16_t(v[k] >> 16));
-        qf[8 + ks][2 * k] = (__bf16)(x1 * cs - x2 * sn);
-        qf[8 + ks][2 * k + 1] = (__bf16)(x1 * sn + x2 * cs);
+        qf[8 + ks][2 * k] = (_Float16)(x1 * cs - x2 * sn);
+        qf[8 + ks][2 * k + 1] = (_Float16)(x1 * sn + x2 * cs);
       }
     }
   }
@@ -293,18 +320,18 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
   };
   // score A operand (rows = tokens): row lane%32, logical chunk 2ks + hi
   const int sr = lane & 31;
-  auto s_op = [&](const lds_u8* tb, int ks) -> bf16x8 {
-    if (ks < 8) return lds16(tb + sr * kRowB + 16 * ((2 * ks + hi) ^ kv_swz(sr)));
-    return lds16(tb + 2 * kTileKB + sr * (kDr * 2) + 16 * ((2 * (ks - 8) + hi) ^ kr_swz(sr)));
+  auto s_op = [&](const lds_u8* tb, int ks) -> f16x8 {
+    if (ks < 8) return lds16h(tb + sr * kRowB + 16 * ((2 * ks + hi) ^ kv_swz(sr)));
+    return lds16h(tb + 2 * kTileKB + sr * (kDr * 2) + 16 * ((2 * (ks - 8) + hi) ^ kr_swz(sr)));
   };
   // weighted-sum A operand V^T for value block db, k-step s: tokens 16s + 4*(g/2) + (lane%16)/4 and
   // +8, value columns 32db + 16(g%2) + 4(lane%4) .. +3 (the token order of the score layout)
-  auto v_op = [&](const lds_u8* tb, int s, int db) -> bf16x8 {
+  auto v_op = [&](const lds_u8* tb, int s, int db) -> f16x8 {
     const int r = 16 * s + 4 * (g >> 1) + (ii >> 2);
     const int col = 32 * db + 16 * (g & 1) + 4 * (ii & 3);
     const lds_u8* vb = tb + kTileKB;
-    return tr_pair(vb + r * kRowB + 16 * ((col >> 3) ^ kv_swz(r)) + 2 * (col & 7),
-                   vb + (r + 8) * kRowB + 16 * ((col >> 3) ^ kv_swz(r + 8)) + 2 * (col & 7));
+    return tr_pair_h(vb + r * kRowB + 16 * ((col >> 3) ^ kv_swz(r)) + 2 * (col & 7),
+                     vb + (r + 8) * kRowB + 16 * ((col >> 3) ^ kv_swz(r + 8)) + 2 * (col & 7));
   };
 
   f32x16 acc[4];
@@ -334,7 +361,7 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
 #pragma unroll
       for (int x = 0; x < 16; ++x) s[x] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s_op(tb, ks), qf[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < 12; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_f16(s_op(tb, ks), qf[ks], s, 0, 0, 0);
 #pragma unroll
       for (int x = 0; x < 16; ++x) s[x] *= qscale;  // base-2 logits
       // mask: tokens past the query's position or the sequence end
@@ -363,25 +390,27 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
           for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
         m_run = m_new;
       }
+      // probabilities times 2^kPShift (at most 2^15, inside binary16), so that weights far below
+      // the maximum stay normal numbers; the factor cancels in out and is taken off lse
       float p[16], tsum = 0.f;
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;  // a query with no visible key yet
+      const float m_use = (m_run == -INFINITY ? 0.f : m_run) - kPShift;  // (no visible key yet: 0)
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         p[x] = fast_exp2(s[x] - m_use);
         tsum += p[x];
       }
       l_lane += tsum;
-      bf16x8 pb0, pb1;
+      f16x8 pb0, pb1;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        pb0[x] = (__bf16)p[x];
-        pb1[x] = (__bf16)p[8 + x];
+        pb0[x] = (_Float16)p[x];
+        pb1[x] = (_Float16)p[8 + x];
       }
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op(tb, sk, db), sk ? pb1 : pb0, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_op(tb, sk, db), sk ? pb1 : pb0, acc[db], 0, 0, 0);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no transfer outlives the workgroup
@@ -401,7 +430,8 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<f32x4*>(o + 32 * db + 8 * q) =
           f32x4{acc[db][4 * q] * inv, acc[db][4 * q + 1] * inv, acc[db][4 * q + 2] * inv, acc[db][4 * q + 3] * inv};
-  if (lse && hi == 0) lse[(size_t(b) * q_len + qi) * kH + h] = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+  if (lse && hi == 0)
+    lse[(size_t(b) * q_len + qi) * kH + h] = empty ? -INFINITY : (m_run + (log2f(l_tot) - kPShift)) * kLn2;
 }
 
 }  // namespace

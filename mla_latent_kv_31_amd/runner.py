@@ -192,9 +192,9 @@ class PrefillUnabsorbedStep:
         self.B, self.Sq = int(inp["q_c"].shape[0]), int(inp["q_c"].shape[1])
         self.max_len = int(max_len or max(1, int(np.max(inp["lens"]))))
         H = w.n_heads
-        self.k = torch.empty((self.B, H, self.max_len, w.d_k), dtype=torch.bfloat16, device=dev)
-        self.v = torch.empty((self.B, H, self.max_len, w.d_v), dtype=torch.bfloat16, device=dev)
-        self.k_r = torch.empty((self.B, self.max_len, w.d_r), dtype=torch.bfloat16, device=dev)
+        self.k = torch.empty((self.B, H, self.max_len, w.d_k), dtype=torch.float16, device=dev)
+        self.v = torch.empty((self.B, H, self.max_len, w.d_v), dtype=torch.float16, device=dev)
+        self.k_r = torch.empty((self.B, self.max_len, w.d_r), dtype=torch.float16, device=dev)
         self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
         self.c = L.cache(self.pool, self.page_table, self.lens)
