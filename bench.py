@@ -244,6 +244,82 @@ def bench_prefill(args, w) -> dict:
     return rec
 
 
+def bench_verify(args, w) -> dict:
+    """Multi-token verify: q_len draft tokens per sequence of a ragged decode batch, each a decode
+    row over its own prefix.  Step: mla_verify_rows -> absorb -> balanced decode -> combine ->
+    out_proj.  The same inputs through mla_prefill_chunk (one workgroup per query row) are timed
+    beside it for comparison."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    inp = gen.make_prefill_inputs(w)
+    dev = torch.device("cuda:0")
+    rows = w.batch * w.q_len
+    qs = inp["q_start"].astype(np.int64)
+    row_lens = np.minimum(np.maximum(qs[:, None] + np.arange(w.q_len)[None, :] + 1, 0),
+                          inp["lens"].astype(np.int64)[:, None])
+    row_bytes = (w.d_c + w.d_r) * 2
+    read_bytes = int(row_lens.sum()) * row_bytes          # every row reads its own prefix
+    unique_bytes = int(inp["lens"].astype(np.int64).sum()) * row_bytes
+    n_units = args.units or runner.balanced_units(row_lens.reshape(-1), runner.compute_units(dev))
+    st = runner.VerifyStep(inp, dev, n_units=n_units)
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        st.rows()
+        st.absorb()
+        ev[i][0].record(stream)
+        st.attend()
+        ev[i][1].record(stream)
+        st.combine()
+        st.out_proj()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    ms_dec = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the same verify through mla_prefill_chunk, for comparison
+    pf = runner.PrefillStep(inp, dev)
+    n_pf = max(5, args.steps // 10)
+    for _ in range(3):
+        pf.run()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n_pf):
+        pf.run()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_pf = start.elapsed_time(stop) / n_pf
+    achieved = read_bytes / (ms_dec * 1e-3) / 1e9
+    flops = int(row_lens.sum()) * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+    return {
+        "metric": "MLA multi-token verify draft tokens/s (V3 shape, 1 GPU)",
+        "value": round(rows / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "draft_tokens": w.q_len, "heads": w.n_heads,
+                   "d_c": w.d_c, "d_r": w.d_r, "rows": rows, "split": f"balanced {n_units} units",
+                   "unique_cache_bytes": unique_bytes, "seed": w.seed},
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_partial_balanced (verify rows)",
+                     "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "ms_per_launch": round(ms_dec, 6), "algorithmic_bytes_per_launch": read_bytes,
+                     "note": "rows of one sequence read the same prefix; repeats may hit L2/MALL"},
+        "roofline_mfma": {"achieved": round(flops / (ms_dec * 1e-3) / 1e12, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(flops / (ms_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "prefill_chunk_ms_per_step": round(ms_pf, 6),
+    }
+
+
 def cpu_baseline_kv_append(inp: dict, seconds: float) -> dict:
     """The fp64 oracle's cache-write steps on rows of the same workload until `seconds` pass."""
     import oracle.mla_oracle as O
@@ -409,8 +485,11 @@ def main() -> int:
     if w.kind == "kv_append":
         print(json.dumps(bench_kv_append(args, w)), flush=True)
         return 0
+    if w.kind == "verify":
+        print(json.dumps(bench_verify(args, w)), flush=True)
+        return 0
     if w.kind != "decode":
-        print(f"workload {w.name} is not a decode, prefill or cache-write workload", file=sys.stderr)
+        print(f"workload {w.name} is not a decode, prefill, verify or cache-write workload", file=sys.stderr)
         return 2
     inp = gen.make_decode_inputs(w)
     dev = torch.device("cuda:0")

@@ -219,6 +219,22 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, const mla_cache* cache, 
 /* Nonzero when the unabsorbed prefill supports these dims. */
 int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims);
 
+/* Multi-token verify (row N4, speculative decoding) through the split-K decode path.  Query i of
+ * sequence b sits at position q_start[b] + i and reads keys t <= q_start[b] + i, t < seq_lens[b]
+ * (the causal rule of a chunk, [ase] causal-mask remark after Fig. 2).  Each such query is a decode
+ * query over its own prefix, so a verify step is decode over batch * q_len rows; this call writes
+ * the rows' description, for row r = b * q_len + i:
+ *   row_table  device int32 [batch * q_len, max_pages]: a copy of page_table row b   (output)
+ *   row_lens   device int32 [batch * q_len]: clamp(q_start[b] + i + 1, 0, seq_lens[b])  (output)
+ *   row_pos    device int32 [batch * q_len] or NULL: q_start[b] + i, the rotary position (output)
+ *   q_start    device int32 [batch]
+ * The rows then form the cache {pool, row_table, row_lens, batch * q_len, page_size, max_pages,
+ * num_pages} for mla_absorb_query (positions row_pos), mla_decode_partial_balanced,
+ * mla_combine_balanced and mla_out_proj, whose outputs are those of mla_prefill_chunk on the same
+ * queries up to rounding.  batch * q_len must not exceed 65535 (MLA_ERR_UNSUPPORTED).  */
+mla_status mla_verify_rows(const mla_cache* cache, const int32_t* q_start, int32_t q_len, int32_t* row_table,
+                           int32_t* row_lens, int32_t* row_pos, void* stream);
+
 /* Query side of one layer ([ase] "현재 토큰의 Query 만들기", Fig. 1; [molayo] query compression):
  *   c^Q = h . W_DQ;  q_c[r,h,:] = c^Q . W_UQ[h];  q_r[r,h,:] = c^Q . W_QR[h]  (unrotated)
  *   h    device dtype [rows, d_model];  w_dq dtype [d_model, d_cq]

@@ -74,6 +74,7 @@ _SIGNATURES = {
     "mla_prefill_unabsorbed_supported": (_I32, [_PD]),
     "mla_kv_append_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
     "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
+    "mla_verify_rows": (_I32, [_PC, _VP, _I32, _VP, _VP, _VP, _VP]),
 }
 
 
@@ -221,6 +222,11 @@ def mla_prefill_unabsorbed(d: MlaDims, c: MlaCache, max_len: int, q_c, q_r, q_st
 
 def mla_prefill_unabsorbed_supported(d: MlaDims) -> bool:
     return bool(library().mla_prefill_unabsorbed_supported(ctypes.byref(d)))
+
+
+def mla_verify_rows(c: MlaCache, q_start, q_len: int, row_table, row_lens, row_pos=None, stream=None) -> None:
+    _check(library().mla_verify_rows(ctypes.byref(c), _addr(q_start), q_len, _addr(row_table), _addr(row_lens),
+                                     _addr(row_pos), _stream(stream)), "mla_verify_rows")
 
 
 def mla_kv_append_workspace_bytes(d: MlaDims, d_model: int, rows: int) -> int:

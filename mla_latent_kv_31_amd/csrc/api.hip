@@ -337,4 +337,18 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
       launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
 }
 
+mla_status mla_verify_rows(const mla_cache* cache, const int32_t* q_start, int32_t q_len, int32_t* row_table,
+                           int32_t* row_lens, int32_t* row_pos, void* stream) {
+  Cache c;
+  MLA_TRY(check_cache(cache, &c));
+  if (q_len < 0) return MLA_ERR_SHAPE;
+  if (int64_t(c.batch) * q_len > 65535) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(q_start));
+  MLA_TRY(ptr_ok(row_table));
+  MLA_TRY(ptr_ok(row_lens));
+  if (row_pos && !aligned16(row_pos)) return MLA_ERR_ALIGN;
+  if (c.batch == 0 || q_len == 0) return MLA_OK;
+  return hip_status(launch_verify_rows(c, q_start, q_len, row_table, row_lens, row_pos, (hipStream_t)stream));
+}
+
 }  // extern "C"

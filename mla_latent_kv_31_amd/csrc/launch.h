@@ -87,4 +87,8 @@ hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const vo
                             const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                             float rms_eps, hipStream_t s);
 
+// Multi-token verify rows for the decode path (verify_rows.hip).
+hipError_t launch_verify_rows(const Cache& c, const int32_t* q_start, int q_len, int32_t* row_table,
+                              int32_t* row_lens, int32_t* row_pos, hipStream_t stream);
+
 }  // namespace mla

@@ -9,6 +9,9 @@ or, with the work-balanced split over ``n_units`` workgroups:
     mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced -> mla_out_proj
 Chunked prefill (q_len query tokens per sequence):
     mla_absorb_query -> mla_prefill_chunk -> mla_out_proj
+Multi-token verify (q_len query tokens per sequence, as batch * q_len decode rows):
+    mla_verify_rows -> mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced
+    -> mla_out_proj
 """
 
 from __future__ import annotations
@@ -167,6 +170,69 @@ class PrefillStep:
     def run(self, stream=None):
         self.absorb(stream)
         self.attend(stream)
+        self.out_proj(stream)
+
+
+class VerifyStep:
+    """Device buffers of one multi-token verify call on the decode path: query i of sequence b
+    becomes decode row b * q_len + i over its own prefix (mla_verify_rows writes the rows' page
+    table, lengths and positions), then the work-balanced decode over ``n_units`` workgroups.
+    Same inputs and outputs as PrefillStep (``out`` [B, q_len, H, d_v], ``lse`` [B, q_len, H])."""
+
+    def __init__(self, inp: dict, device="cuda:0", n_units: int = 256, flags: int = 0):
+        w = inp["workload"]
+        self.w = w
+        self.device = torch.device(device)
+        self.d = dims_for(w, flags)
+        dev = self.device
+        self.q_c = to_device(inp["q_c"], dev)
+        self.q_r = to_device(inp["q_r"], dev)
+        self.w_uk = to_device(inp["w_uk"], dev)
+        self.w_uv = to_device(inp["w_uv"], dev)
+        self.pool = to_device(inp["pool"], dev)
+        self.page_table = to_device(inp["page_table"], dev)
+        self.lens = to_device(inp["lens"].astype(np.int32), dev)
+        self.q_start = to_device(inp["q_start"].astype(np.int32), dev)
+        self.B, self.Sq = int(inp["q_c"].shape[0]), int(inp["q_c"].shape[1])
+        R = self.B * self.Sq
+        H, W = w.n_heads, w.d_c + w.d_r
+        self.n_units = int(n_units)
+        max_pages = int(self.page_table.shape[1])
+        self.row_table = torch.empty((R, max_pages), dtype=torch.int32, device=dev)
+        self.row_lens = torch.empty((R,), dtype=torch.int32, device=dev)
+        self.row_pos = torch.empty((R,), dtype=torch.int32, device=dev)
+        self.S = L.mla_balanced_num_slots(R, self.n_units)
+        td = _torch_dtype(w.dtype)
+        self.q_hat = torch.empty((R, H, W), dtype=td, device=dev)
+        self.o_part = torch.empty((max(self.S, 1), H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((max(self.S, 1), H), dtype=torch.float32, device=dev)
+        self.z = torch.empty((self.B, self.Sq, H, w.d_c), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
+        self.c = L.cache(self.pool, self.page_table, self.lens)
+        self.rc = L.cache(self.pool, self.row_table, self.row_lens, batch=R, page_size=int(self.pool.shape[1]),
+                          max_pages=max_pages, num_pages=int(self.pool.shape[0]))
+
+    def rows(self, stream=None):
+        L.mla_verify_rows(self.c, self.q_start, self.Sq, self.row_table, self.row_lens, self.row_pos, stream)
+
+    def absorb(self, stream=None):
+        L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.row_pos, self.B * self.Sq, self.q_hat, stream)
+
+    def attend(self, stream=None):
+        L.mla_decode_partial_balanced(self.d, self.rc, self.q_hat, self.n_units, self.o_part, self.lse_part, stream)
+
+    def combine(self, stream=None):
+        L.mla_combine_balanced(self.d, self.rc, self.n_units, self.o_part, self.lse_part, self.z, self.lse, stream)
+
+    def out_proj(self, stream=None):
+        L.mla_out_proj(self.d, self.z, self.w_uv, self.B * self.Sq, self.out, stream)
+
+    def run(self, stream=None):
+        self.rows(stream)
+        self.absorb(stream)
+        self.attend(stream)
+        self.combine(stream)
         self.out_proj(stream)
 
 

@@ -55,7 +55,7 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 class Workload:
     name: str
     seed: int
-    kind: str                       # "toy" | "decode" | "prefill" | "kv_append"
+    kind: str                       # "toy" | "decode" | "prefill" | "kv_append" | "verify" (prefill inputs)
     batch: int
     n_heads: int = 128
     d_c: int = 512
@@ -110,10 +110,16 @@ WORKLOADS: dict[str, Workload] = {
         name="v3_kv_append_prefill_b2", seed=7, kind="kv_append", batch=2, ctx=2048, q_len=512,
         random_pages=True, d_model=4096,
         notes="the 512-token chunk of each of 2 sequences, written at positions 2048..2559"),
+    # multi-token verify (speculative decoding): 4 draft tokens per sequence of the ragged batch
+    "v3_verify_b64_sq4": Workload(
+        name="v3_verify_b64_sq4", seed=8, kind="verify", batch=64, ctx_range=(1024, 32768), q_len=4,
+        random_pages=True,
+        notes="64 sequences with prior lengths uniform on [1024, 32768] plus 4 draft tokens each, "
+              "already appended; 64-token pages, random page table"),
 }
 
 WORKLOAD_ORDER = ["toy_fp32", "v3_b1_ctx4k", "v3_b64_ragged_paged", "v3_b4_ctx128k", "v3_prefill_b2",
-                  "v3_kv_append_b64", "v3_kv_append_prefill_b2"]
+                  "v3_kv_append_b64", "v3_kv_append_prefill_b2", "v3_verify_b64_sq4"]
 
 
 # --------------------------------------------------------------------------
@@ -236,12 +242,18 @@ def make_prefill_inputs(w: Workload, *, seed: int | None = None, fill: str = "ra
     """Inputs for one chunked-prefill call: prior ctx tokens plus q_len new tokens.
 
     The new chunk's own rows are already in the cache (cache length ctx + q_len per sequence).
-    Query i of sequence b sits at absolute position q_start[b] + i with q_start = ctx.
-    Draw order: W_UK, W_UV, latent rows, k^R rows, q_C, q_R, page permutation, fills.
+    Query i of sequence b sits at absolute position q_start[b] + i with q_start = the prior length
+    (ctx, or drawn uniformly from ctx_range per sequence when the workload gives one).
+    Draw order: [prior lengths], W_UK, W_UV, latent rows, k^R rows, q_C, q_R, page permutation, fills.
     """
     rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
     H, dc, dr, dk, dv = w.n_heads, w.d_c, w.d_r, w.d_k, w.d_v
-    lens = np.full(w.batch, w.ctx + w.q_len, dtype=np.int32)
+    if w.ctx_range is not None:
+        lo, hi = w.ctx_range
+        prior = rng.integers(lo, hi + 1, size=w.batch, dtype=np.int64).astype(np.int32)
+    else:
+        prior = np.full(w.batch, w.ctx, dtype=np.int32)
+    lens = (prior + w.q_len).astype(np.int32)
     w_uk = _normal(rng, (H, dc, dk), 1.0 / math.sqrt(dc))
     w_uv = _normal(rng, (H, dc, dv), 1.0 / math.sqrt(dc))
     rows = []
@@ -255,7 +267,7 @@ def make_prefill_inputs(w: Workload, *, seed: int | None = None, fill: str = "ra
     pool, table = paginate(rows, w.page_size, rng=rng, random_pages=w.random_pages,
                            spare_pages=spare_pages, fill=fill, dtype=w.dtype)
     return dict(workload=w, dtype=w.dtype, lens=lens,
-                q_start=np.full(w.batch, w.ctx, dtype=np.int32),
+                q_start=prior.copy(),
                 q_c=_store(q_c, w.dtype), q_r=_store(q_r, w.dtype),
                 w_uk=_store(w_uk, w.dtype), w_uv=_store(w_uv, w.dtype),
                 pool=pool, page_table=table)

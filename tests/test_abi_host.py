@@ -185,3 +185,22 @@ def test_kv_append_workspace_validation():
     assert call(nbytes=need - 4) == M.MLA_ERR_SHAPE
     assert call(ws=U) == M.MLA_ERR_ALIGN
     assert call(rows=0, ws=None, nbytes=0) == M.MLA_OK
+
+
+def test_verify_rows_validation():
+    lib = M.library()
+    c = _cache()
+
+    def call(cache=c, q_start=A, q_len=4, table=B_, lens=B_, pos=None):
+        return lib.mla_verify_rows(ctypes.byref(cache) if cache is not None else None, q_start, q_len, table, lens,
+                                   pos, None)
+
+    assert call(cache=None) == M.MLA_ERR_NULL
+    assert call(q_start=None) == M.MLA_ERR_NULL
+    assert call(table=None) == M.MLA_ERR_NULL
+    assert call(lens=U) == M.MLA_ERR_ALIGN
+    assert call(pos=U) == M.MLA_ERR_ALIGN
+    assert call(q_len=-1) == M.MLA_ERR_SHAPE
+    assert call(cache=_cache(batch=20000), q_len=4) == M.MLA_ERR_UNSUPPORTED  # 80,000 rows
+    assert call(q_len=0) == M.MLA_OK
+    assert call(cache=_cache(batch=0)) == M.MLA_OK
