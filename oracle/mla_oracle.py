@@ -30,6 +30,11 @@ Conventions (readings where the pages differ or are silent):
   * 0-based absolute positions; a query at position p sees keys j <= p ([ase] causal-mask remark
     after Fig. 2)
   * an empty key set gives z = 0, o = 0, lse = -inf
+  * FP8 latent cache ([huny] section 5, FP8 item): E4M3 as the OCP 8-bit floating-point format
+    defines it, one scale per token over its 512 latent values, taken as the smallest power of
+    two that brings the largest magnitude within 448 (the page names per-tensor or per-token
+    scales and fixes no rule; a power of two keeps code value x scale exact); the rotary key
+    stays bf16
 
 Parity pins for every function live in tests/ (oracle pins, invariants and planted-mistake
 tests); none of the functions below is parity unpinned.
@@ -358,6 +363,109 @@ def attention_loops(q_c, q_r, q_pos, cache, w_uk, w_uv, d_c, scale=None, base=10
                     val += cache[j][c] * w_uv[h][c][v]
                 o[h][v] += a * val
     return dict(o=np.array(o), z=np.array(z), lse=np.array(lse))
+
+
+# --------------------------------------------------------------------------
+# FP8 latent cache ([huny] section 5, FP8 mixed-precision item: E4M3 on the 512-wide latent with
+# a per-token scale factor)
+# --------------------------------------------------------------------------
+# E4M3 as the OCP 8-bit floating-point format defines it (the "FN" variant): sign, 4 exponent
+# bits with bias 7, 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; no infinities;
+# S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+E4M3_MAX = 448.0
+FP8_ROW_BYTES = 656  # 512 codes | 64 bf16 rotary values | fp32 scale | 12 zero bytes
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of every E4M3 code (uint8 array) as float64; NaN codes give NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(F64)))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def _half_even(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest integer, ties to even (x >= 0)."""
+    f = np.floor(x)
+    d = x - f
+    up = (d > 0.5) | ((d == 0.5) & (np.fmod(f, 2.0) == 1.0))
+    return f + up
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code to each value, ties to the even code; |x| must not exceed 448 (the
+    quantiser's scale guarantees it).  Zero keeps its sign; NaN gives 0x7F."""
+    x = np.asarray(x, dtype=F64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("value beyond the E4M3 range")
+    a = np.abs(np.nan_to_num(x, nan=0.0))
+    code = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: multiples of 2^-9 (a result of 8 steps is the smallest normal, code 0x08)
+    code = np.where(sub, _half_even(a / 2.0 ** -9).astype(np.int64), code)
+    # normal range: a = (1 + k/8) * 2^E, E = floor(log2 a); k = 8 carries into the exponent
+    E = np.floor(np.log2(np.where(sub, 1.0, a)))
+    # guard the floor of log2 against its own rounding at exact powers of two
+    E = np.where(np.exp2(E) > a, E - 1, E)
+    E = np.where(np.exp2(E + 1) <= a, E + 1, E)
+    k = _half_even((a / np.exp2(E) - 1.0) * 8.0).astype(np.int64)
+    norm_code = (((E + 7).astype(np.int64)) << 3) + k  # k = 8 rolls into the next exponent
+    code = np.where(sub, code, norm_code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def fp8_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Per-token scale 2^e with the smallest integer e such that amax <= 448 * 2^e, so the scaled
+    latent fills the E4M3 range; an all-zero latent takes e = 0.  A power of two keeps
+    code value * scale exact in any binary format that holds it."""
+    amax = np.asarray(amax, dtype=F64)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    pos = amax > 0
+    est = np.ceil(np.log2(np.where(pos, amax, 1.0) / E4M3_MAX)).astype(np.int64)
+    # settle the estimate exactly: smallest e with amax <= 448 * 2^e
+    est = np.where(amax > E4M3_MAX * np.exp2(est.astype(F64)), est + 1, est)
+    est = np.where(amax <= E4M3_MAX * np.exp2((est - 1).astype(F64)), est - 1, est)
+    return np.where(pos, est, e)
+
+
+def quantize_latents_fp8(c: np.ndarray):
+    """Per-token E4M3 quantisation of latent rows c [N, d_c]: returns (codes uint8 [N, d_c],
+    scale float64 [N]) with codes = E4M3(c / scale) and scale = 2^e (fp8_scale_exponent of the
+    row's largest magnitude).  Division by a power of two is exact."""
+    c = np.asarray(c, dtype=F64)
+    e = fp8_scale_exponent(np.max(np.abs(c), axis=-1))
+    scale = np.exp2(e.astype(F64))
+    return e4m3_encode(c / scale[..., None]), scale
+
+
+def dequantize_latents_fp8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Latent values the FP8 cache holds: code value times the token's scale (exact in fp64)."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=F64)[..., None]
+
+
+def fp8_rows_pack(codes: np.ndarray, kr_bf16_bits: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Byte image of FP8 cache rows [N, 656]: the d_c codes, the rotary key's bf16 bit patterns
+    (unchanged), the scale as a little-endian float32, zero padding to a 16-byte multiple."""
+    n = codes.shape[0]
+    out = np.zeros((n, FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :512] = codes
+    out[:, 512:640] = np.ascontiguousarray(kr_bf16_bits, dtype=np.uint16).view(np.uint8).reshape(n, 128)
+    out[:, 640:644] = np.asarray(scale, dtype=np.float32).reshape(n, 1).view(np.uint8)
+    return out
+
+
+def fp8_rows_unpack(rows: np.ndarray):
+    """Inverse of fp8_rows_pack: (codes [N, 512], rotary bf16 bits [N, 64], scale float64 [N])."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    codes = rows[:, :512].copy()
+    kr = rows[:, 512:640].copy().view(np.uint16).reshape(n, 64)
+    scale = rows[:, 640:644].copy().view(np.float32).reshape(n).astype(F64)
+    return codes, kr, scale
 
 
 # --------------------------------------------------------------------------

@@ -375,10 +375,68 @@ def pin_projections():
         _close(res["o"][hd], ref, 1e-12, f"toy head {hd}")
 
 
+def pin_fp8_e4m3():
+    """E4M3 against what the format and a library routine fix: the values of characteristic codes
+    (OCP 8-bit floating point, E4M3: bias 7, subnormals m * 2^-9, S.1111.111 NaN, largest 448),
+    every code's value against torch's float8_e4m3fn, the nearest-even encoding of random values,
+    of every code value and of every midpoint against torch's cast, and the round trip."""
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+             0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for code, val in fixed.items():
+        got = float(O.e4m3_decode(np.array([code], np.uint8))[0])
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), f"code {code:#04x}: {got} != {val}"
+    assert np.isnan(O.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all(), "NaN codes"
+    codes = np.arange(256, dtype=np.uint8)
+    val = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(val), nan) and np.array_equal(val[~nan], ref[~nan]), "decode vs torch"
+    fin = np.sort(val[~nan])
+    r = _rng(41)
+    x = np.concatenate([r.uniform(-448, 448, 4000), r.standard_normal(4000) * np.exp2(r.integers(-12, 8, 4000)),
+                        fin, (fin[:-1] + fin[1:]) / 2]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    got = O.e4m3_encode(x.astype(np.float64))
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want), f"encode vs torch: {int(np.sum(got != want))} codes differ"
+    ok = codes[~nan]
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(ok)), ok), "round trip"
+
+
+def pin_fp8_scale_and_rows():
+    """The per-token scale rule by brute force (smallest e with amax <= 448 * 2^e), quantisation
+    error within half a code step, the scaled maximum inside the range, and the row byte image."""
+    for amax in (448.0, 448.0 * (1 + 2.0 ** -20), 224.0, 1.0, 0.875, 3.0e-5, 1.0e4, 0.0):
+        e = int(O.fp8_scale_exponent(np.array([amax]))[0])
+        if amax == 0.0:
+            assert e == 0
+            continue
+        best = next(k for k in range(-200, 200) if amax <= 448.0 * 2.0 ** k)
+        assert e == best, f"scale exponent of {amax}: {e} != {best}"
+    r = _rng(42)
+    c = r.standard_normal((9, 512)) * np.exp2(r.integers(-8, 8, (9, 1)))
+    c[3] = 0.0
+    codes, scale = O.quantize_latents_fp8(c)
+    deq = O.dequantize_latents_fp8(codes, scale)
+    assert np.all(np.abs(c / scale[:, None]) <= 448.0)
+    assert np.all(np.max(np.abs(c), axis=1)[[0, 1, 2, 4]] > 224.0 * scale[[0, 1, 2, 4]]), "scale is the smallest"
+    # each value within half the spacing of its binade: 2^-4 relative (normal), 2^-10 * scale (subnormal)
+    half_step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(c), 1e-300))) - 4), 2.0 ** -10 * scale[:, None])
+    assert np.all(np.abs(deq - c) <= half_step), "quantisation error beyond half a step"
+    assert np.all(deq[3] == 0.0) and scale[3] == 1.0
+    kr = gen.bf16_bits(r.standard_normal((9, 64)).astype(np.float32))
+    rows = O.fp8_rows_pack(codes, kr, scale)
+    assert rows.shape == (9, 656) and np.all(rows[:, 644:] == 0)
+    assert np.array_equal(rows[0, :512], codes[0]) and rows[0, 512:514].view(np.uint16)[0] == kr[0, 0]
+    assert rows[1, 640:644].view(np.float32)[0] == np.float32(scale[1])
+    c2, k2, s2 = O.fp8_rows_unpack(rows)
+    assert np.array_equal(c2, codes) and np.array_equal(k2, kr) and np.array_equal(s2, scale)
+
+
 ALL_PINS = {f.__name__: f for f in (
     pin_score_example, pin_key_absorption, pin_value_absorption, pin_cache_accounting,
     pin_rope_closed_forms, pin_rope_complex_form, pin_rope_relative,
     pin_sdpa_textbook, pin_sdpa_general, pin_prefill_causal, pin_loops_twin,
     pin_absorbed_equals_decompressed, pin_softmax_and_special_cases, pin_merge_partials,
-    pin_gather_rows, pin_projections,
+    pin_gather_rows, pin_projections, pin_fp8_e4m3, pin_fp8_scale_and_rows,
 )}

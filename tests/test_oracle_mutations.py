@@ -80,7 +80,33 @@ def _gather_wrong(pool, table, b, length):
     return out
 
 
+def _e4m3_decode_bias8(codes):
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(F64)
+    mag = np.where(e == 0, m * 2.0 ** -10, (1.0 + m / 8.0) * np.exp2((e - 8).astype(F64)))
+    return np.where((c & 0x7F) == 0x7F, np.nan, np.where(c & 0x80, -mag, mag))
+
+
+_real_encode = O.e4m3_encode
+
+
+def _e4m3_encode_truncating(x):
+    x = np.asarray(x, F64)
+    lo = _real_encode(x)
+    # step toward zero where the nearest code lies above the magnitude
+    over = np.abs(O.e4m3_decode(lo)) > np.abs(x)
+    return np.where(over & ((lo & 0x7F) > 0), lo - 1, lo).astype(np.uint8)
+
+
+def _scale_exponent_floor(amax):
+    amax = np.asarray(amax, F64)
+    return np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0).astype(np.int64)
+
+
 MUTANTS = {
+    "e4m3_exponent_bias_8": ("e4m3_decode", _e4m3_decode_bias8),
+    "e4m3_truncates": ("e4m3_encode", _e4m3_encode_truncating),
+    "fp8_scale_rounds_down": ("fp8_scale_exponent", _scale_exponent_floor),
     "rope_opposite_sign": ("rope", _rope_neg),
     "rope_half_split_pairs": ("rope", _rope_half_split),
     "rope_frequency_exponent": ("rope_inv_freq", _inv_freq_half),
