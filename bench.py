@@ -455,6 +455,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/decode_traffic_<workload>.json from two rocprofv3 --pmc runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="decode workloads: FP8 latent cache (the bf16 pool quantised on the GPU first)")
     ap.add_argument("--unabsorbed", action="store_true",
                     help="prefill workloads: time the unabsorbed path (decompress + attend) instead")
     args = ap.parse_args()
@@ -475,6 +477,7 @@ def main() -> int:
     import numpy as np
     import torch
 
+    from mla_latent_kv_31_amd import _lib as L
     from mla_latent_kv_31_amd import runner
     from mla_workloads import gen
 
@@ -499,14 +502,25 @@ def main() -> int:
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    flags = 0
+    inp_dev = inp
+    if args.fp8:  # FP8 rows of the same latents, quantised on the GPU (mla_quantize_rows_fp8)
+        P, ps, _ = inp["pool"].shape
+        src = runner.to_device(inp["pool"], dev)
+        pool8 = torch.empty((P, ps, L.MLA_FP8_ROW_BYTES), dtype=torch.uint8, device=dev)
+        L.mla_quantize_rows_fp8(runner.dims_for(w), src, P * ps, pool8)
+        torch.cuda.synchronize()
+        del src
+        inp_dev = dict(inp, pool=pool8)
+        flags = L.MLA_FLAG_CACHE_FP8
     if args.split_tokens:
-        st = runner.DecodeStep(inp, args.split_tokens, dev)
+        st = runner.DecodeStep(inp_dev, args.split_tokens, dev, flags=flags)
     else:
         n_units = args.units or runner.balanced_units(inp["lens"], runner.compute_units(dev))
-        st = runner.DecodeStep(inp, 0, dev, n_units=n_units)
+        st = runner.DecodeStep(inp_dev, 0, dev, n_units=n_units, flags=flags)
     lens = inp["lens"].astype(np.int64)
     total_tokens = int(lens.sum())
-    row_bytes = (w.d_c + w.d_r) * 2
+    row_bytes = L.MLA_FP8_ROW_BYTES if args.fp8 else (w.d_c + w.d_r) * 2
     cache_bytes = total_tokens * row_bytes
     flops_decode = total_tokens * (2 * w.n_heads * (w.d_c + w.d_r) + 2 * w.n_heads * w.d_c)
     flops_proj = w.batch * 2 * w.n_heads * w.d_c * (w.d_k + w.d_v)
@@ -536,10 +550,10 @@ def main() -> int:
     ms_decode = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     sha = _kernel_sha()
-    traffic = _traffic(w.name, sha)
+    traffic = None if args.fp8 else _traffic(w.name, sha)
     achieved = cache_bytes / (ms_decode * 1e-3) / 1e9
     rec = {
-        "metric": "MLA decode cache GB/s (V3 shape, 1 GPU)",
+        "metric": "MLA decode cache GB/s (V3 shape, 1 GPU)" + (", FP8 cache" if args.fp8 else ""),
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 3),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -555,7 +569,8 @@ def main() -> int:
                    "d_k": w.d_k, "d_v": w.d_v, "page_size": w.page_size,
                    "split": f"fixed {st.split_tokens}" if st.n_units is None else f"balanced {st.n_units} units",
                    "partials": st.S * (st.B if st.n_units is None else 1), "cache_tokens": total_tokens, "seed": w.seed,
-                   "decode_kernel": "mfma" if st.uses_mfma() else "generic"},
+                   "decode_kernel": "mfma" if st.uses_mfma() else "generic",
+                   "cache_format": "fp8 e4m3, 656 B rows" if args.fp8 else "bf16, 1,152 B rows"},
         "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "cache_tokens_per_s": round(total_tokens / (ms_step * 1e-3), 1),
         "tflops": round((flops_decode + flops_proj) / (ms_step * 1e-3) / 1e12, 3),

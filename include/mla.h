@@ -46,6 +46,19 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 /* Flags for mla_dims.flags. */
 #define MLA_FLAG_FORCE_GENERIC 1 /* use the dimension-generic kernels even where a tuned one exists */
+/* The cache pool holds FP8 rows (row N1; [huny] section 5, FP8 mixed-precision item: E4M3 on the
+ * 512-wide latent with a per-token scale).  Row of MLA_FP8_ROW_BYTES bytes:
+ *   bytes   0..511  E4M3 codes of c / 2^e (OCP 8-bit E4M3: bias 7, subnormals m * 2^-9, largest
+ *                   finite 448; nearest-even), e the smallest integer with max|c| <= 448 * 2^e
+ *   bytes 512..639  the 64 rotary values k^R, bf16, unchanged
+ *   bytes 640..643  the scale 2^e as a float32;  bytes 644..655 zero
+ * The cache then holds code value x 2^e, exact in bf16, and every kernel reads those values.
+ * Honoured by mla_decode_partial(_balanced), mla_prefill_chunk (through the bf16 MFMA kernels for
+ * d_c 512, d_r 64, 128 heads) and mla_kv_append (its MFMA path); elsewhere, or for other shapes,
+ * the calls return MLA_ERR_UNSUPPORTED.  Latent rows whose largest magnitude is below 2^-110 are
+ * outside the supported range (their scale would leave the float32 normal range). */
+#define MLA_FLAG_CACHE_FP8 2
+#define MLA_FP8_ROW_BYTES 656
 
 /* Model dimensions shared by every call.
  * Cached row of one token: [c^KV (d_c) | k^R (d_r)], k^R already rotated at its position and
@@ -218,6 +231,12 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, const mla_cache* cache, 
                                   const void* v, const void* k_r, float* out, float* lse, void* stream);
 /* Nonzero when the unabsorbed prefill supports these dims. */
 int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims);
+
+/* bf16 cache rows -> FP8 cache rows (MLA_FLAG_CACHE_FP8 layout), row by row; the scale of each row
+ * comes from its own 512 latent values.  src device bf16 [rows, 576]; dst device bytes
+ * [rows, MLA_FP8_ROW_BYTES].  Only d_c 512, d_r 64 in bf16 (else MLA_ERR_UNSUPPORTED).  Rows holding
+ * non-finite values give unspecified codes (never read: slots past a sequence's length). */
+mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t rows, void* dst, void* stream);
 
 /* Multi-token verify (row N4, speculative decoding) through the split-K decode path.  Query i of
  * sequence b sits at position q_start[b] + i and reads keys t <= q_start[b] + i, t < seq_lens[b]

@@ -25,6 +25,8 @@ MLA_ERR_HIP = 6
 MLA_F32 = 0
 MLA_BF16 = 1
 MLA_FLAG_FORCE_GENERIC = 1
+MLA_FLAG_CACHE_FP8 = 2
+MLA_FP8_ROW_BYTES = 656
 
 # Balanced split-K constants (include/mla.h)
 MLA_BALANCED_TILE = 32
@@ -75,6 +77,7 @@ _SIGNATURES = {
     "mla_kv_append_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
     "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
     "mla_verify_rows": (_I32, [_PC, _VP, _I32, _VP, _VP, _VP, _VP]),
+    "mla_quantize_rows_fp8": (_I32, [_PD, _VP, ctypes.c_int64, _VP, _VP]),
 }
 
 
@@ -222,6 +225,11 @@ def mla_prefill_unabsorbed(d: MlaDims, c: MlaCache, max_len: int, q_c, q_r, q_st
 
 def mla_prefill_unabsorbed_supported(d: MlaDims) -> bool:
     return bool(library().mla_prefill_unabsorbed_supported(ctypes.byref(d)))
+
+
+def mla_quantize_rows_fp8(d: MlaDims, src, rows: int, dst, stream=None) -> None:
+    _check(library().mla_quantize_rows_fp8(ctypes.byref(d), _addr(src), rows, _addr(dst), _stream(stream)),
+           "mla_quantize_rows_fp8")
 
 
 def mla_verify_rows(c: MlaCache, q_start, q_len: int, row_table, row_lens, row_pos=None, stream=None) -> None:

@@ -67,6 +67,9 @@ mla_status ptr_ok(const void* p) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+bool cache_fp8(const mla_dims* dims) { return (dims->flags & MLA_FLAG_CACHE_FP8) != 0; }
+bool generic_forced(const mla_dims* dims) { return (dims->flags & MLA_FLAG_FORCE_GENERIC) != 0; }
+
 #define MLA_TRY(expr)                 \
   do {                                \
     mla_status _st = (expr);          \
@@ -143,9 +146,12 @@ mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, cons
   if (split_tokens < 1 || split_tokens % c.page_size != 0) return MLA_ERR_SHAPE;
   if (max_len < 0 || int64_t(max_len) > int64_t(c.max_pages) * c.page_size) return MLA_ERR_SHAPE;
   const int S = mla_decode_num_splits(max_len, split_tokens);
+  const bool mfma = !generic_forced(dims) && decode_mfma_supported(d, c, split_tokens);
+  if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0) return MLA_OK;
-  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && decode_mfma_supported(d, c, split_tokens))
-    return hip_status(launch_decode_mfma(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
+  if (mfma)
+    return hip_status(launch_decode_mfma(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream,
+                                         cache_fp8(dims)));
   return hip_status(launch_decode_generic(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
 }
 
@@ -180,9 +186,12 @@ mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* ca
   MLA_TRY(ptr_ok(q_hat));
   MLA_TRY(ptr_ok(o_part));
   MLA_TRY(ptr_ok(lse_part));
+  const bool mfma = !generic_forced(dims) && decode_mfma_supported(d, c, 0);
+  if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0) return MLA_OK;
-  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && decode_mfma_supported(d, c, 0))
-    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream));
+  if (mfma)
+    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream,
+                                                  cache_fp8(dims)));
   return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream));
 }
 
@@ -229,10 +238,12 @@ mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const
   MLA_TRY(ptr_ok(q_start));
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  const bool mfma = !generic_forced(dims) && prefill_mfma_supported(d, c);
+  if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0 || q_len == 0) return MLA_OK;
   if (int64_t(c.batch) * q_len > (int64_t(1) << 31) - 1) return MLA_ERR_UNSUPPORTED;
-  if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && prefill_mfma_supported(d, c))
-    return hip_status(launch_prefill_mfma(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream));
+  if (mfma)
+    return hip_status(launch_prefill_mfma(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream, cache_fp8(dims)));
   return hip_status(launch_prefill_generic(d, c, q_hat, q_len, q_start, z, lse, (hipStream_t)stream));
 }
 
@@ -265,7 +276,7 @@ mla_status mla_decompress_kv(const mla_dims* dims, const mla_cache* cache, int32
   Cache c;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
-  if (!prefill_unabsorbed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_unabsorbed_supported(d) || cache_fp8(dims)) return MLA_ERR_UNSUPPORTED;
   if (max_len < 1) return MLA_ERR_SHAPE;
   if (int64_t(c.batch) * d.H * int64_t(max_len) * d.dk > (int64_t(1) << 40)) return MLA_ERR_UNSUPPORTED;
   MLA_TRY(ptr_ok(w_uk));
@@ -284,7 +295,7 @@ mla_status mla_prefill_unabsorbed(const mla_dims* dims, const mla_cache* cache, 
   Cache c;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
-  if (!prefill_unabsorbed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_unabsorbed_supported(d) || cache_fp8(dims)) return MLA_ERR_UNSUPPORTED;
   if (max_len < 1 || q_len < 0) return MLA_ERR_SHAPE;
   if (int64_t(c.batch) * d.H * int64_t(max_len) * d.dk > (int64_t(1) << 40)) return MLA_ERR_UNSUPPORTED;
   MLA_TRY(ptr_ok(q_c));
@@ -319,6 +330,7 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
   MLA_TRY(check_cache(cache, &c));
   if (d_model < 1 || rows < 0 || !(rms_eps == rms_eps)) return MLA_ERR_SHAPE;
   const bool mfma = kv_append_uses_mfma(dims, d, d_model);
+  if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (!mfma && d_model + d.dc + d.dr > 8192) return MLA_ERR_UNSUPPORTED;
   if (mfma && int64_t(rows) * d_model > (int64_t(1) << 31) - 1) return MLA_ERR_UNSUPPORTED;
   MLA_TRY(ptr_ok(h));
@@ -331,10 +343,22 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
     MLA_TRY(ptr_ok(workspace));
     if (workspace_bytes < kv_append_mfma_workspace(d_model, rows)) return MLA_ERR_SHAPE;
     return hip_status(launch_kv_append_mfma(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps,
-                                            workspace, (hipStream_t)stream));
+                                            workspace, (hipStream_t)stream, cache_fp8(dims)));
   }
   return hip_status(
       launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
+}
+
+mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t rows, void* dst, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (d.dtype != MLA_BF16 || d.dc != 512 || d.dr != 64) return MLA_ERR_UNSUPPORTED;
+  if (rows < 0) return MLA_ERR_SHAPE;
+  if (rows > (int64_t(1) << 33)) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(src));
+  MLA_TRY(ptr_ok(dst));
+  if (rows == 0) return MLA_OK;
+  return hip_status(launch_quantize_rows_fp8(src, rows, dst, (hipStream_t)stream));
 }
 
 mla_status mla_verify_rows(const mla_cache* cache, const int32_t* q_start, int32_t q_len, int32_t* row_table,

@@ -92,6 +92,20 @@ constexpr int kPvOps = 2 * kMBlk;                // 16 transposed operands per t
 constexpr int kPvSteps = 2 * kPvOps;             // 32 weighted-sum MFMAs per tile
 constexpr float kRerunMargin = 64.0f;  // reference may lag the running max by this much
 
+// FP8 cache rows (E4M3 latent codes with one power-of-two scale per token): 512 codes | 64 bf16
+// rotary values | fp32 scale | 12 zero bytes.  The FP8 variant of the kernel stages each tile's
+// codes (and scales) in LDS, converts them once per tile into the bf16 tile layout above, and runs
+// the unchanged MFMA phases on that.  Three bf16 tile buffers (tile j scored, tile j-1 summed,
+// tile j+1 being converted) and two code staging slots fit next to the exchange buffers.
+constexpr int kRowB8 = 656;
+constexpr int kNBuf8 = 3;
+constexpr int kStgCodesB = kTile * kDc;           // 16 KiB of codes per staged tile
+constexpr int kStgB = kStgCodesB + 1024;          // + one transfer of the 32 rows' scale chunks
+constexpr int kStgOff = kNBuf8 * kTileB;
+constexpr int kXOff8 = kStgOff + 2 * kStgB;
+constexpr int kLdsB8 = kXOff8 + 2 * kXBufB;       // 158 KiB
+static_assert(kLdsB8 <= 160 * 1024, "FP8 layout fits the CU's LDS");
+
 __host__ __device__ constexpr int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __host__ __device__ constexpr int rope_swz(int row) { return (row >> 1) & 7; }
 
@@ -148,7 +162,7 @@ enum Mode {
                   // straight to z / lse; grid = rows, longest rows first
 };
 
-template <int MODE>
+template <int MODE, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __restrict__ page_table,
                         const int32_t* __restrict__ seq_lens, int batch, int max_pages, int page_size,
@@ -156,7 +170,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
                         int split_tokens, const int32_t* __restrict__ q_start, float* __restrict__ o_part,
                         float* __restrict__ lse_part) {
   constexpr bool kBal = MODE == kBalanced;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsB];
+  constexpr int kNB = F8 ? kNBuf8 : kNBuf;          // bf16 tile buffers
+  constexpr int kXO = F8 ? kXOff8 : kXOff;          // exchange buffers
+  __shared__ __attribute__((aligned(16))) unsigned char smem[F8 ? kLdsB8 : kLdsB];
   lds_u8* const lbase = (lds_u8*)smem;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -176,7 +192,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     return lane16 ^ uint32_t(16 * lat_swz(4 * (x & 3) + wave_u));
   };
   auto rope_off = [&]() {
-    return uint32_t((lane >> 3) * kRowB + kLatB + 16 * ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)));
+    constexpr int rb = F8 ? kRowB8 : kRowB, ro = F8 ? kDc : kLatB;  // row stride, rotary offset
+    return uint32_t((lane >> 3) * rb + ro + 16 * ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)));
   };
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lbase));
 
@@ -203,8 +220,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     pv_d8 = 8 * kLatB + 16 * (((4 + y) ^ lat_swz(8 + r0)) - ((4 + y) ^ lat_swz(r0)));
   }
   // probability exchange: this lane's 16 bytes of k-step s in the buffer of tile parity t
-  const uint32_t x_mine = uint32_t(kXOff + wave * kXWaveB + 16 * lane);
-  const uint32_t x_peer = uint32_t(kXOff + (wave ^ 1) * kXWaveB + 16 * lane);
+  const uint32_t x_mine = uint32_t(kXO + wave * kXWaveB + 16 * lane);
+  const uint32_t x_peer = uint32_t(kXO + (wave ^ 1) * kXWaveB + 16 * lane);
   auto x_at = [&](uint32_t base, int t, int s) { return lbase + base + t * kXBufB + s * 1024; };
   auto a_src = [&](const lds_u8* tb, int kk) -> const lds_u8* {
     return kk < kDc / 16 ? tb + 256 * (kk >> 3) + (qk_x ^ (32 * (kk & 7))) : tb + (qr_x ^ (32 * (kk & 3)));
@@ -291,7 +308,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       const int kt = kt0 + k;
       const int pg = __builtin_amdgcn_readlane(my_page, ((kt >> tiles_per_page_log2) - p0 - wbase) & 63);
       const int in_page = (kt & ((1 << tiles_per_page_log2) - 1)) * kTile;
-      return reinterpret_cast<const unsigned char*>(pool + (size_t(pg) * page_size + in_page) * kW);
+      if constexpr (F8)
+        return reinterpret_cast<const unsigned char*>(pool) + (size_t(pg) * page_size + in_page) * kRowB8;
+      else
+        return reinterpret_cast<const unsigned char*>(pool + (size_t(pg) * page_size + in_page) * kW);
     };
     auto dma_one = [&](const unsigned char* g, uint32_t dst, int x) {  // x-th transfer of a tile
       if (x < kLatPerWave) {
@@ -303,12 +323,78 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     };
     auto dma_tile = [&](int k) {
       const unsigned char* g = tile_src(k);
-      const uint32_t dst = lds0 + uint32_t((k % kNBuf) * kTileB);
+      const uint32_t dst = lds0 + uint32_t((k % kNB) * kTileB);
 #pragma unroll
       for (int x = 0; x < kDmaPerWave; ++x) dma_one(g, dst, x);
     };
+    // ---- FP8: transfer x of a tile's codes and scales into staging slot `slot`.  Transfer
+    // T = 4*wave + x (x < 4) moves rows 2T, 2T+1 (512 code bytes each; lane L: row 2T + L/32, chunk
+    // L%32); x = 4 (wave 0 only) moves the 16-byte scale chunk of row L%32 (lanes 32..63 repeat
+    // rows 0..31).  The rotary rows go straight into the bf16 tile buffer (dma_rope8).
+    const uint32_t c8_off = uint32_t((lane >> 5) * kRowB8 + 16 * (lane & 31));
+    const uint32_t s8_off = uint32_t((lane & 31) * kRowB8 + kDc + 2 * (kW - kDc));
+    auto dma_codes8 = [&](const unsigned char* g, int slot, int x) {
+      const uint32_t dst = lds0 + uint32_t(kStgOff + slot * kStgB);
+      if (x < 4) {
+        const int T = 4 * wave_u + x;
+        dma16(dst + uint32_t(T * 1024), c8_off, g + size_t(2 * T) * kRowB8);
+      } else if (wave_u == 0) {
+        dma16(dst + uint32_t(kStgCodesB), s8_off, g);
+      }
+    };
+    auto dma_rope8 = [&](const unsigned char* g, int k) {
+      dma16(lds0 + uint32_t((k % kNB) * kTileB + kRopeOff + wave_u * 1024), rope_off(), g + size_t(8 * wave_u) * kRowB8);
+    };
+    auto dma_tile8 = [&](int k) {  // codes and scales of tile k into slot k&1, its rotary rows into buffer k%3
+      const unsigned char* g = tile_src(k);
+#pragma unroll
+      for (int x = 0; x < 5; ++x) dma_codes8(g, k & 1, x);
+      dma_rope8(g, k);
+    };
+    // ---- FP8: convert the staged codes of tile k (slot k&1) into the bf16 latent rows of buffer
+    // k%3, code x scale (exact: a power-of-two scale), rows >= nval as zeros.  Wave w converts rows
+    // 8w..8w+7; lane l takes row 8w + l/8 and code chunks q = l%8 + 8u (16 codes, two bf16 chunks).
+    const int cv_row = 8 * wave + (lane >> 3);
+    auto cv_read = [&](int k, int u) {  // 16 codes of chunk u
+      const lds_u8* stg = lbase + kStgOff + (k & 1) * kStgB;
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stg + cv_row * kDc +
+                                                                                16 * ((lane & 7) + 8 * u));
+    };
+    auto cv_scale = [&](int k) {
+      const lds_u8* stg = lbase + kStgOff + (k & 1) * kStgB + kStgCodesB;
+      return *reinterpret_cast<const __attribute__((address_space(3))) float*>(stg + 16 * cv_row);
+    };
+    // the two bf16 output chunks (8 values each) of code chunk u, half h (dwords 2h, 2h+1)
+    auto cv_write = [&](int k, int u, int h, const u32x4& codes, float scale, bool valid) {
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t w = codes[2 * h + d];
+        o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false));
+        o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true));
+      }
+      if (!valid) o = u32x4{0u, 0u, 0u, 0u};
+      const int c = 2 * ((lane & 7) + 8 * u) + h;  // bf16 chunk of the 1,024-byte latent row
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          lbase + (k % kNB) * kTileB + cv_row * kLatB + 256 * (c >> 4) + 16 * ((c & 15) ^ lat_swz(cv_row))) = o;
+    };
+    auto cv_valid = [&](int k) { return cv_row < t1 - (t0 + k * kTile); };
+    auto convert_tile8 = [&](int k) {  // all at once (the prologue's tile 0)
+      const float sc = cv_scale(k);
+      const bool v = cv_valid(k);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 cd = cv_read(k, u);
+        cv_write(k, u, 0, cd, sc, v);
+        cv_write(k, u, 1, cd, sc, v);
+      }
+    };
 
-    dma_tile(0);
+    if constexpr (F8) {
+      dma_tile8(0);
+    } else {
+      dma_tile(0);
+    }
 
     // ---- this wave's 32 heads of q_hat, as the B operand of S^T = tile . q_hat^T, held in
     // registers for the whole segment: 32 latent and 4 rotary k-steps.
@@ -328,7 +414,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     for (int k = 0; k < kKLat; ++k) asm volatile("" : "+v"(qf[k]));
 #pragma unroll
     for (int k = 0; k < kKSteps - kKLat; ++k) asm volatile("" : "+v"(rq[k]));
-    if (ntiles > 1) dma_tile(1);
+    if constexpr (F8) {
+      // codes of tile 1 (past a one-tile segment: a copy of tile 0 into the free slot)
+      const unsigned char* g1 = tile_src(min(1, ntiles - 1));
+#pragma unroll
+      for (int x = 0; x < 5; ++x) dma_codes8(g1, 1, x);
+    } else {
+      if (ntiles > 1) dma_tile(1);
+    }
 
     f32x16 acc[kAcc];  // acc[2 * mb + 0]: own heads, acc[2 * mb + 1]: the partner's
     float m_ref = -INFINITY, m_max = -INFINITY, l_lane = 0.f;
@@ -340,12 +433,22 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
           wbase = 0;
           my_page = load_page_window(pt_row, p0, npg, max_pages, lane);
         }
-        dma_tile(0);
-        if (ntiles > 1) dma_tile(1);
+        if constexpr (F8) {
+          dma_tile8(0);
+          const unsigned char* g1 = tile_src(min(1, ntiles - 1));
+#pragma unroll
+          for (int x = 0; x < 5; ++x) dma_codes8(g1, 1, x);
+        } else {
+          dma_tile(0);
+          if (ntiles > 1) dma_tile(1);
+        }
       }
       // source of the transfers issued in the next tile step: tile j+2 of step j, or, past the
       // segment end, a harmless copy of its last tile into the buffer that is free anyway
       const unsigned char* g_dma = tile_src(min(2, ntiles - 1));
+      // FP8: source of tile j+1, whose rotary rows go out at the top of step j (its address was
+      // the code transfers' source one step earlier, taken before any page-window move)
+      const unsigned char* g_rope = F8 ? tile_src(min(1, ntiles - 1)) : nullptr;
 #pragma unroll
       for (int a = 0; a < kAcc; ++a)
 #pragma unroll
@@ -362,9 +465,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       {
         const u32x4 zero = {0u, 0u, 0u, 0u};
         for (int x = threadIdx.x; x < kRopeOff / 16; x += kThreads)
-          *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + (kNBuf - 1) * kTileB + 16 * x) = zero;
+          *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(lbase + (kNB - 1) * kTileB + 16 * x) = zero;
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(x_at(x_mine, 1, 0)) = zero;
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(x_at(x_mine, 1, 1)) = zero;
+      }
+      if constexpr (F8) {  // tile 0's codes landed: convert them before the loop
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        convert_tile8(0);
       }
 
       bool over = false;
@@ -376,18 +484,22 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
           wbase += 64;
           my_page = load_page_window(pt_row, p0 + wbase, npg - wbase, max_pages, lane);
         }
-        if (j + 1 < ntiles)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");  // tile j landed, j+1 may fly
+        if (F8 || j + 1 >= ntiles)
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // FP8: codes of j+1 and rotary rows of j landed
         else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerWave) : "memory");  // tile j landed, j+1 may fly
         __syncthreads();  // every wave's part of tile j landed; tile j-2 fully consumed
         // Keep the per-step offsets derived inside the loop (one XOR each) instead of letting the
         // compiler hoist a dozen precomputed copies into registers next to the q_hat fragments.
         asm volatile("" : "+v"(qk_x), "+v"(qr_x), "+v"(pv_x), "+v"(pv_d8), "+v"(lane16));
-        lds_u8* const tb = lbase + (j % kNBuf) * kTileB;
-        lds_u8* const tp = lbase + ((j + kNBuf - 1) % kNBuf) * kTileB;
+        lds_u8* const tb = lbase + (j % kNB) * kTileB;
+        lds_u8* const tp = lbase + ((j + kNB - 1) % kNB) * kTileB;
         const int nvalid = min(kTile, t1 - (t0 + j * kTile));
-        if (nvalid < kTile) {  // tail tile: latent rows past the sequence end read as zeros
+        // FP8: the rotary rows of tile j+1 go to the buffer tile j-2 left (past the segment end a
+        // copy of the last tile's); its latent rows are converted in phase B below
+        if constexpr (F8) dma_rope8(g_rope, j + 1);
+        if (!F8 && nvalid < kTile) {  // tail tile: latent rows past the sequence end read as zeros
+          // (FP8 tiles get their zero rows from the conversion)
           const u32x4 zero = {0u, 0u, 0u, 0u};
           for (int x = threadIdx.x; x < (kTile - nvalid) * (kLatB / 16); x += kThreads)
             *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(tb + nvalid * kLatB + 16 * x) = zero;
@@ -396,7 +508,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         // Tile j+2 goes to the buffer that tile j-2 left; past the segment end the transfers copy
         // the segment's last tile there instead, which keeps the wait counts uniform and the loop
         // free of branches.  Every transfer lands before the loop ends (drained below).
-        const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNBuf) * kTileB);
+        const uint32_t dnext = lds0 + uint32_t(((j + 2) % kNB) * kTileB);
         const unsigned char* g_dma_next = g_dma;
 
         // ---- phase A: scores of tile j, one dependent MFMA chain, operands read kQA steps
@@ -422,7 +534,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
             if (i == kDmaPerWave + 2) pq0 = lds16(x_at(x_peer, (j + 1) & 1, 0));
             if (i == kDmaPerWave + 3) pq1 = lds16(x_at(x_peer, (j + 1) & 1, 1));
             score_step(i == 0, i == kKSteps - 1, sacc, qa[i % (kQA + 1)], i < kKLat ? qf[i] : rq[i - kKLat]);
-            if (i % 4 == 1) dma_one(g_dma, dnext, i / 4);
+            if constexpr (F8) {
+              if (i % 4 == 1 && i / 4 < 5) dma_codes8(g_dma, j & 1, i / 4);  // codes of tile j+2
+            } else {
+              if (i % 4 == 1) dma_one(g_dma, dnext, i / 4);
+            }
             if (i == 22) g_dma_next = tile_src(min(j + 3, ntiles - 1));  // for the next step
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -445,6 +561,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
           const bool first = pass == 0 && j == 0;  // the segment's first tile fixes the reference
           float mx0 = 0.f, mx = 0.f, pr[16], tsum = 0.f;
           bf16x8 pn0, pn1;
+          u32x4 cv_cd[2];  // FP8: code chunks of tile j+1 in flight
+          float cv_sc = 0.f;
+          bool cv_ok = false;
 #pragma unroll
           for (int i = 0; i < kPvSteps; ++i) {
             const int o = i >> 1, nb = i & 1;  // operand, head block (0: own, 1: partner)
@@ -484,10 +603,22 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
             // for the partner, read after the next tile's barrier
             if (i == 13) *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(x_at(x_mine, j & 1, 0)) = pn0;
             if (i == 21) *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(x_at(x_mine, j & 1, 1)) = pn1;
+            if constexpr (F8) {
+              // the codes of tile j+1 become its bf16 latent rows in the shadow of the last
+              // weighted-sum MFMAs, once the scores and probabilities are dead: chunk u is read two
+              // steps before its two halves are converted and written (steps 20 .. 27)
+              if (i == 17) {
+                cv_sc = cv_scale(j + 1);
+                cv_ok = cv_valid(j + 1);
+              }
+              if (i >= 20 && i < 28) cv_write(j + 1, (i - 20) >> 1, i & 1, cv_cd[((i - 20) >> 1) & 1], cv_sc, cv_ok);
+              if (i >= 18 && i < 26 && !(i & 1)) cv_cd[((i - 18) >> 1) & 1] = cv_read(j + 1, (i - 18) >> 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
           pb0 = pn0;
           pb1 = pn1;
+          if constexpr (F8) g_rope = g_dma;
           g_dma = g_dma_next;
         }
       }
@@ -496,7 +627,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       {
-        lds_u8* const tp = lbase + ((ntiles - 1) % kNBuf) * kTileB;
+        lds_u8* const tp = lbase + ((ntiles - 1) % kNB) * kTileB;
         const bf16x8 pq0 = lds16(x_at(x_peer, (ntiles - 1) & 1, 0));
         const bf16x8 pq1 = lds16(x_at(x_peer, (ntiles - 1) & 1, 1));
         bf16x8 pa[3];
@@ -516,7 +647,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       // ---- rerun the segment if some head outgrew its reference (uniform decision)
       // the flags go to the buffer after the last tile's, idle now
       __attribute__((address_space(3))) int* rerun_flag =
-          reinterpret_cast<__attribute__((address_space(3))) int*>(lbase + (ntiles % kNBuf) * kTileB);
+          reinterpret_cast<__attribute__((address_space(3))) int*>(lbase + (ntiles % kNB) * kTileB);
       const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
       if (lane == 0) rerun_flag[wave] = wave_over;
       __syncthreads();
@@ -532,13 +663,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     // every store instruction writes 1 KiB of one contiguous half row instead.
     const float l_tot = lane_swap_sum(l_lane);
     __attribute__((address_space(3))) float* const l_x =
-        reinterpret_cast<__attribute__((address_space(3))) float*>(lbase + kXOff + (ntiles & 1) * kXBufB);
+        reinterpret_cast<__attribute__((address_space(3))) float*>(lbase + kXO + (ntiles & 1) * kXBufB);
     if (hi == 0) l_x[head] = l_tot;
     __syncthreads();  // every wave is done with the tile buffers and the rerun flags; sums published
     const float inv_own = 1.f / l_tot, inv_peer = 1.f / l_x[(wave ^ 1) * 32 + (lane & 31)];
     {
       constexpr int kStRow = 256 * 4 + 16;  // one staged half row, padded against bank conflicts
-      static_assert(kWaves * 32 * kStRow <= kXOff, "staging stays clear of the exchange buffers");
+      static_assert(kWaves * 32 * kStRow <= kXOff && kWaves * 32 * kStRow <= kXOff8,
+                    "staging stays clear of the exchange buffers");
       lds_u8* const stg = lbase + wave * 32 * kStRow;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {  // head block: own, then the partner's
@@ -577,20 +709,22 @@ bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens) {
 }
 
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
-                              float* o_part, float* lse_part, hipStream_t s) {
+                              float* o_part, float* lse_part, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<kFixed><<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
+  auto k = fp8 ? decode_mfma_kernel<kFixed, true> : decode_mfma_kernel<kFixed, false>;
+  k<<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), n_splits, split_tokens, nullptr, o_part, lse_part);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
-                                       float* lse_part, hipStream_t s) {
+                                       float* lse_part, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<kBalanced><<<dim3(n_units), kThreads, 0, s>>>(
+  auto k = fp8 ? decode_mfma_kernel<kBalanced, true> : decode_mfma_kernel<kBalanced, false>;
+  k<<<dim3(n_units), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), n_units, 0, nullptr, o_part, lse_part);
   return hipGetLastError();
@@ -599,10 +733,11 @@ hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void
 bool prefill_mfma_supported(const Dims& d, const Cache& c) { return decode_mfma_supported(d, c, 0); }
 
 hipError_t launch_prefill_mfma(const Dims& d, const Cache& c, const void* q_hat, int q_len, const int32_t* q_start,
-                               float* z, float* lse, hipStream_t s) {
+                               float* z, float* lse, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  decode_mfma_kernel<kPrefill><<<dim3(c.batch * q_len), kThreads, 0, s>>>(
+  auto k = fp8 ? decode_mfma_kernel<kPrefill, true> : decode_mfma_kernel<kPrefill, false>;
+  k<<<dim3(c.batch * q_len), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), q_len, 0, q_start, z, lse);
   return hipGetLastError();

@@ -24,6 +24,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace mla {
@@ -143,6 +144,7 @@ struct InvFreq {
 
 constexpr int kFinishWaves = 4;  // waves per row in the finish: they share out the K splits
 
+template <bool F8>
 __global__ __launch_bounds__(64 * kFinishWaves) void kv_finish_kernel(const float* __restrict__ part, int rows,
                                                                      int splits, Cache c,
                                                                      const int32_t* __restrict__ seq_ids,
@@ -182,13 +184,36 @@ __global__ __launch_bounds__(64 * kFinishWaves) void kv_finish_kernel(const floa
   const float scale = rms_eps > 0.f ? 1.f / sqrtf(ss / float(kDc) + rms_eps) : 1.f;
 
   const int b = seq_ids[r], t = positions[r];
-  uint16_t* row = const_cast<uint16_t*>(static_cast<const uint16_t*>(c.pool)) +
-                  row_index(c.page_table, c.max_pages, c.page_size, b, t) * kW;
-  u32x4 o;
+  uint16_t* row;
+  if constexpr (F8) {
+    // E4M3 codes of the normalised fp32 latent under the token's power-of-two scale (fp8.h)
+    unsigned char* row8 = const_cast<unsigned char*>(static_cast<const unsigned char*>(c.pool)) +
+                          row_index(c.page_table, c.max_pages, c.page_size, b, t) * kFp8RowB;
+    float amax = 0.f;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-    o[x] = uint32_t(f32_to_bf16(v[2 * x] * scale)) | (uint32_t(f32_to_bf16(v[2 * x + 1] * scale)) << 16);
-  *reinterpret_cast<u32x4*>(row + 8 * lane) = o;
+    for (int x = 0; x < 8; ++x) {
+      v[x] *= scale;
+      amax = fmaxf(amax, fabsf(v[x]));
+    }
+    const int e = fp8_scale_exp(wave_max(amax));
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      w0 |= e4m3_code(ldexpf(v[x], -e)) << (8 * x);
+      w1 |= e4m3_code(ldexpf(v[4 + x], -e)) << (8 * x);
+    }
+    *reinterpret_cast<uint2*>(row8 + 8 * lane) = make_uint2(w0, w1);
+    if (lane == 0) *reinterpret_cast<u32x4*>(row8 + kFp8ScaleOff) = u32x4{__float_as_uint(ldexpf(1.f, e)), 0u, 0u, 0u};
+    row = reinterpret_cast<uint16_t*>(row8);  // the rotary values follow the 512 code bytes
+  } else {
+    row = const_cast<uint16_t*>(static_cast<const uint16_t*>(c.pool)) +
+          row_index(c.page_table, c.max_pages, c.page_size, b, t) * kW;
+    u32x4 o;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      o[x] = uint32_t(f32_to_bf16(v[2 * x] * scale)) | (uint32_t(f32_to_bf16(v[2 * x + 1] * scale)) << 16);
+    *reinterpret_cast<u32x4*>(row + 8 * lane) = o;
+  }
   if (lane < kDr / 2) {
     // angle pos * base^(-2i/d_r), i = lane, in double, reduced to [-pi, pi] before the float32
     // sine and cosine
@@ -197,7 +222,9 @@ __global__ __launch_bounds__(64 * kFinishWaves) void kv_finish_kernel(const floa
     float sn, cn;
     sincosf(float(rd), &sn, &cn);
     const float r1 = k1 * cn - k2 * sn, r2 = k1 * sn + k2 * cn;
-    *reinterpret_cast<uint32_t*>(row + kDc + 2 * lane) = uint32_t(f32_to_bf16(r1)) | (uint32_t(f32_to_bf16(r2)) << 16);
+    // (bf16 rotary values start at element 512 of a bf16 row, byte 512 of an FP8 row)
+    uint16_t* kr = F8 ? row + kDc / 2 : row + kDc;
+    *reinterpret_cast<uint32_t*>(kr + 2 * lane) = uint32_t(f32_to_bf16(r1)) | (uint32_t(f32_to_bf16(r2)) << 16);
   }
 }
 
@@ -225,7 +252,7 @@ size_t kv_append_mfma_workspace(int d_model, int rows) {
 
 hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                                  const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
-                                 float rms_eps, float* workspace, hipStream_t s) {
+                                 float rms_eps, float* workspace, hipStream_t s, bool fp8) {
   const int splits = kv_splits(d_model, rows);
   const dim3 grid(kColTiles, (rows + kRowsWg - 1) / kRowsWg, splits);
   kv_gemm_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(h), d_model, rows,
@@ -235,7 +262,8 @@ hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, con
   if (e != hipSuccess) return e;
   InvFreq inv;
   for (int i = 0; i < kDr / 2; ++i) inv.v[i] = pow(double(d.rope_base), -2.0 * i / kDr);
-  kv_finish_kernel<<<rows, 64 * kFinishWaves, 0, s>>>(workspace, rows, splits, c, seq_ids, positions, rms_eps, inv);
+  auto fin = fp8 ? kv_finish_kernel<true> : kv_finish_kernel<false>;
+  fin<<<rows, 64 * kFinishWaves, 0, s>>>(workspace, rows, splits, c, seq_ids, positions, rms_eps, inv);
   return hipGetLastError();
 }
 

@@ -32,13 +32,13 @@ constexpr int kGenericMaxDk = 1024;
 // split_tokens == 0 asks about the balanced split.
 bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens);
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
-                              float* o_part, float* lse_part, hipStream_t s);
+                              float* o_part, float* lse_part, hipStream_t s, bool fp8 = false);
 hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
-                                       float* lse_part, hipStream_t s);
+                                       float* lse_part, hipStream_t s, bool fp8 = false);
 // chunked prefill on the same kernel: one workgroup per query row over its causal key range
 bool prefill_mfma_supported(const Dims& d, const Cache& c);
 hipError_t launch_prefill_mfma(const Dims& d, const Cache& c, const void* q_hat, int q_len, const int32_t* q_start,
-                               float* z, float* lse, hipStream_t s);
+                               float* z, float* lse, hipStream_t s, bool fp8 = false);
 
 // ---- bf16 MFMA per-head projections (d_c 512, d_k = d_v = 128) and the vectorised combine
 bool proj_mfma_supported(const Dims& d);
@@ -82,10 +82,13 @@ bool kv_append_mfma_supported(const Dims& d, int d_model);
 size_t kv_append_mfma_workspace(int d_model, int rows);
 hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                                  const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
-                                 float rms_eps, float* workspace, hipStream_t s);
+                                 float rms_eps, float* workspace, hipStream_t s, bool fp8 = false);
 hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                             const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                             float rms_eps, hipStream_t s);
+
+// bf16 cache rows [rows, 576] -> FP8 cache rows [rows, 656 bytes] (fp8_quantize.hip).
+hipError_t launch_quantize_rows_fp8(const void* src, int64_t rows, void* dst, hipStream_t stream);
 
 // Multi-token verify rows for the decode path (verify_rows.hip).
 hipError_t launch_verify_rows(const Cache& c, const int32_t* q_start, int q_len, int32_t* row_table,

@@ -23,7 +23,10 @@ from . import _lib as L
 
 
 def to_device(x: np.ndarray, device) -> torch.Tensor:
-    """Host array -> device tensor.  uint16 arrays are bfloat16 bit patterns."""
+    """Host array -> device tensor.  uint16 arrays are bfloat16 bit patterns; a tensor already on
+    the device is used as it is."""
+    if isinstance(x, torch.Tensor):
+        return x.to(device)
     x = np.ascontiguousarray(x)
     if x.dtype == np.uint16:
         return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)

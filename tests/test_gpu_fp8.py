@@ -1,0 +1,247 @@
+"""GPU parity of the FP8 latent cache (MLA_FLAG_CACHE_FP8; [huny] section 5, FP8 mixed-precision
+item: E4M3 on the 512-wide latent with a per-token scale).
+
+* mla_quantize_rows_fp8 (bf16 rows -> 656-byte FP8 rows) must equal the oracle's quantisation
+  byte for byte: the codes are integers decided from the same bf16 values in exact arithmetic.
+* The decode, the balanced decode and the prefill over an FP8 pool must match the oracle run on
+  the latents that pool holds (code value x scale, dequantised by the oracle from its own
+  quantisation), with the bf16 tolerances of the absorbed path.  Because code value x 2^e is
+  exact in bf16, the FP8 decode must also be bitwise identical to the bf16 decode over a pool
+  that holds those values.
+* mla_kv_append with the flag writes FP8 rows: its latents come from fp32 sums, the oracle's from
+  fp64, so every stored value must lie within half a code step of the oracle's latent (plus
+  1e-5 relative), the scale must be the oracle's, and rows not written keep their bytes.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_31_amd as M
+import oracle.mla_oracle as O
+from mla_latent_kv_31_amd import runner
+from mla_workloads import gen
+from parity import TOL, OracleView, assert_abs_close, assert_mid_close, assert_rms_close, note
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F8 = M.MLA_FLAG_CACHE_FP8
+HEADS = [0, 77, 127]
+
+
+def _np(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def oracle_fp8_rows(rows):
+    """[N, 576] bf16 bit patterns -> [N, 656] FP8 rows, by the oracle."""
+    codes, scale = O.quantize_latents_fp8(gen.as_f64(rows[:, :512], "bf16"))
+    return O.fp8_rows_pack(codes, rows[:, 512:], scale)
+
+
+def oracle_fp8_pool(pool):
+    P, ps, _ = pool.shape
+    return oracle_fp8_rows(pool.reshape(-1, pool.shape[2])).reshape(P, ps, O.FP8_ROW_BYTES)
+
+
+def dequantized_bf16_pool(pool8):
+    """bf16 pool holding exactly the values of an FP8 pool (code value x 2^e is a bf16 value)."""
+    P, ps, _ = pool8.shape
+    codes, kr, scale = O.fp8_rows_unpack(pool8.reshape(-1, O.FP8_ROW_BYTES))
+    table = O.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float32)
+    lat = table[codes] * scale.astype(np.float32)[:, None]
+    bits = (lat.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bits.astype(np.uint32) << 16, lat.view(np.uint32)), "dequantised values are bf16"
+    return np.concatenate([bits, kr], axis=1).reshape(P, ps, 576)
+
+
+class Fp8View(OracleView):
+    """Oracle over the latents an FP8 pool holds."""
+
+    def __init__(self, inp, pool8):
+        super().__init__(inp)
+        self.pool8 = pool8
+
+    def cache(self, b, length=None):
+        L = int(self.inp["lens"][b]) if length is None else length
+        codes, kr, scale = O.fp8_rows_unpack(O.gather_rows(self.pool8, self.inp["page_table"], b, L))
+        return np.concatenate([O.dequantize_latents_fp8(codes, scale), gen.as_f64(kr, "bf16")], axis=1)
+
+
+def _quantize_gpu(rows):
+    src = runner.to_device(rows, DEV)
+    dst = torch.zeros((rows.shape[0], O.FP8_ROW_BYTES), dtype=torch.uint8, device=DEV)
+    M.mla_quantize_rows_fp8(runner.dims_for(gen.WORKLOADS["v3_b1_ctx4k"]), src, rows.shape[0], dst)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def test_quantize_rows_bit_exact():
+    """Random rows over 40 binades, an all-zero row, rows whose maximum sits exactly on or next to a
+    scale boundary (448 * 2^k, 1.75 * 2^k), signed zeros, values down in the subnormal codes, and a
+    row count off the four-row workgroup."""
+    rng = np.random.Generator(np.random.PCG64(71))
+    n = 4096 + 37
+    x = rng.standard_normal((n, 576)).astype(np.float32) * np.exp2(rng.integers(-20, 20, (n, 1))).astype(np.float32)
+    x[5, :512] = 0.0
+    x[6, :512] = -0.0
+    x[7, 3] = 448.0 * 2.0 ** 5
+    x[8, 9] = -1.75 * 2.0 ** -3
+    x[9, 100] = np.nextafter(np.float32(1.75), np.float32(2.0)) * 2.0 ** 4
+    x[10, :512] *= 2.0 ** -12       # most values far below the row maximum: subnormal codes
+    x[10, 0] = 1.0
+    rows = gen.bf16_bits(x)
+    note(f"quantize {n} rows")
+    got = _quantize_gpu(rows)
+    want = oracle_fp8_rows(rows)
+    bad = np.nonzero(np.any(got != want, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
+
+
+def _small_decode_inputs():
+    w = gen.Workload(name="fp8_small", seed=72, kind="decode", batch=7, ctx_range=(1, 300), random_pages=True)
+    lens = np.array([1, 31, 32, 33, 65, 200, 300], np.int32)
+    return gen.make_decode_inputs(w, lens=lens)
+
+
+@pytest.mark.parametrize("mode", ["balanced", "fixed"])
+def test_fp8_decode_small_ragged(mode):
+    """Lengths around the 32-token tile and the 64-token page, every sequence on three heads
+    against the oracle; every output bitwise against the bf16 decode of the dequantised pool."""
+    inp = _small_decode_inputs()
+    pool8 = oracle_fp8_pool(inp["pool"])
+    inp8 = dict(inp, pool=pool8)
+    inpb = dict(inp, pool=dequantized_bf16_pool(pool8))
+    kw = dict(n_units=8) if mode == "balanced" else dict(split_tokens=64)
+    note(f"fp8 decode small ragged {mode}")
+    st8 = runner.DecodeStep(inp8, device=DEV, flags=F8, **kw)
+    stb = runner.DecodeStep(inpb, device=DEV, **kw)
+    assert st8.uses_mfma()
+    st8.run()
+    stb.run()
+    torch.cuda.synchronize()
+    for name in ("z", "lse", "out"):
+        a, b = getattr(st8, name).cpu().numpy(), getattr(stb, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{name}: FP8 and bf16-of-FP8 differ"
+    view = Fp8View(inp8, pool8)
+    tol = TOL["bf16"]
+    for b in range(len(inp["lens"])):
+        ref = view.decode(b, heads=HEADS)
+        assert_mid_close(_np(st8.z)[b, HEADS], ref["z"][HEADS], "bf16", f"z seq {b}")
+        assert_abs_close(_np(st8.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
+        assert_rms_close(_np(st8.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
+
+
+def test_fp8_decode_v3_ragged_sampled():
+    """The serving-scale batch (64 ragged sequences, 1k-32k tokens): the pool quantised on the GPU;
+    for sampled sequences their rows equal the oracle's quantisation byte for byte, and the decode
+    matches the oracle over those rows (three heads)."""
+    inp = gen.make_decode_inputs(gen.WORKLOADS["v3_b64_ragged_paged"])
+    P, ps, _ = inp["pool"].shape
+    note("fp8 decode v3_b64_ragged_paged")
+    pool8 = _quantize_gpu(inp["pool"].reshape(-1, 576)).reshape(P, ps, O.FP8_ROW_BYTES)
+    inp8 = dict(inp, pool=pool8)
+    st = runner.DecodeStep(inp8, device=DEV, flags=F8, n_units=256)
+    st.run()
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    longest = int(np.argmax(inp["lens"]))
+    for b in sorted({0, 13, longest, 63}):
+        L = int(inp["lens"][b])
+        rows_bf16 = O.gather_rows(inp["pool"], inp["page_table"], b, L)
+        mine = oracle_fp8_rows(rows_bf16)
+        assert np.array_equal(O.gather_rows(pool8, inp["page_table"], b, L), mine), f"seq {b}: quantised rows"
+        codes, kr, scale = O.fp8_rows_unpack(mine)
+        cache = np.concatenate([O.dequantize_latents_fp8(codes, scale), gen.as_f64(kr, "bf16")], axis=1)
+        ref = O.attention(gen.as_f64(inp["q_c"][b], "bf16"), gen.as_f64(inp["q_r"][b], "bf16"), L - 1, cache,
+                          gen.as_f64(inp["w_uk"], "bf16"), gen.as_f64(inp["w_uv"], "bf16"), 512, heads=HEADS)
+        assert_abs_close(_np(st.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
+        assert_rms_close(_np(st.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
+
+
+def test_fp8_prefill_small():
+    """The chunked prefill over an FP8 pool: every row of a ragged-start chunk on three heads."""
+    w = gen.Workload(name="fp8_prefill", seed=73, kind="prefill", batch=3, ctx=70, q_len=24, random_pages=True)
+    inp = gen.make_prefill_inputs(w)
+    inp["q_start"] = np.array([70, 0, 13], np.int32)
+    pool8 = oracle_fp8_pool(inp["pool"])
+    inp8 = dict(inp, pool=pool8)
+    note("fp8 prefill small")
+    st = runner.PrefillStep(inp8, DEV, flags=F8)
+    st.run()
+    torch.cuda.synchronize()
+    view = Fp8View(inp8, pool8)
+    tol = TOL["bf16"]
+    for b in range(3):
+        for i in range(w.q_len):
+            ref = view.prefill_row(b, i, HEADS)
+            assert_abs_close(_np(st.lse)[b, i, HEADS], ref["lse"][HEADS], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i, HEADS], ref["o"][HEADS], tol, f"o ({b},{i})")
+
+
+@pytest.mark.parametrize("name,rows,d_model", [("v3_kv_append_b64", None, None), ("kv_edge", 37, 768)])
+def test_fp8_kv_append(name, rows, d_model):
+    """FP8 cache write: stored codes within half a code step of the oracle's latent, the oracle's
+    scale, the rotary values as in the bf16 path, untouched rows unchanged."""
+    base = gen.WORKLOADS["v3_kv_append_b64"]
+    w = base if rows is None else gen.Workload(name=name, seed=74, kind="kv_append", batch=base.batch,
+                                               ctx_range=base.ctx_range, q_len=3, random_pages=True,
+                                               d_model=d_model)
+    t = gen.make_kv_append_inputs(w) if rows is None else gen.make_kv_append_inputs(w, rows=rows)
+    R = t["h"].shape[0]
+    P, ps, _ = t["pool"].shape
+    rng = np.random.Generator(np.random.PCG64(75))
+    pool0 = rng.integers(0, 256, (P, ps, O.FP8_ROW_BYTES), dtype=np.uint8)
+    note(f"fp8 kv_append {name} rows={R} d_model={w.d_model}")
+    d = runner.dims_for(w, F8)
+    dev = lambda a: runner.to_device(a, DEV)  # noqa: E731
+    # the descriptor holds raw device addresses: keep every tensor it names alive until the end
+    pool = dev(pool0)
+    table = dev(t["page_table"])
+    lens = dev(np.zeros(w.batch, np.int32))
+    c = M.cache(pool, table, lens)
+    ws_bytes = M.mla_kv_append_workspace_bytes(d, w.d_model, R)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=DEV)
+    M.mla_kv_append(d, c, w.d_model, dev(t["h"]), dev(t["w_dkv"]), dev(t["w_kr"]), dev(t["seq_ids"]),
+                    dev(t["positions"]), R, 1e-6, ws, ws_bytes)
+    torch.cuda.synchronize()
+    after = pool.cpu().numpy()
+    pages = t["page_table"][t["seq_ids"], t["positions"] // ps]
+    slots = t["positions"] % ps
+    codes, kr, scale = O.fp8_rows_unpack(after[pages, slots])
+    h = gen.as_f64(t["h"], "bf16")
+    c_ref = O.rms_normalize(O.kv_latent(h, gen.as_f64(t["w_dkv"], "bf16")), 1e-6)
+    _, scale_ref = O.quantize_latents_fp8(c_ref)
+    assert np.array_equal(scale, scale_ref), "per-token scales"
+    got = O.dequantize_latents_fp8(codes, scale)
+    half_step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(c_ref), 1e-300))) - 4),
+                           2.0 ** -10 * scale[:, None])
+    excess = np.abs(got - c_ref) - (half_step + 1e-5 * np.abs(c_ref))
+    assert excess.max() <= 0, f"latent codes: worst excess {excess.max():.3e}"
+    kr_ref = O.rope_key(h, gen.as_f64(t["w_kr"], "bf16"), t["positions"], w.rope_base)
+    kr_got = gen.as_f64(kr, "bf16")
+    rms = math.sqrt(float(np.mean(kr_ref ** 2)))
+    assert np.all(np.abs(kr_got - kr_ref) <= 2.0 ** -8 * np.abs(kr_ref) + 1e-4 * rms), "rotary values"
+    assert np.all(after[pages, slots][:, 644:] == 0)
+    untouched = np.ones((P, ps), dtype=bool)
+    untouched[pages, slots] = False
+    assert np.array_equal(after[untouched], pool0[untouched]), "rows that were not written changed"
+
+
+def test_fp8_unsupported_paths():
+    """The FP8 flag on the unabsorbed prefill, or with the generic kernels forced, is refused."""
+    w = gen.WORKLOADS["v3_prefill_b2"]
+    d = runner.dims_for(w, F8)
+    x = torch.zeros(16, dtype=torch.float32, device=DEV)
+    pool = torch.zeros((1, 64, 656), dtype=torch.uint8, device=DEV)
+    table = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    lens = torch.ones(1, dtype=torch.int32, device=DEV)
+    c = M.cache(pool, table, lens)
+    with pytest.raises(M.MlaError):
+        M.mla_decompress_kv(d, c, 64, x, x, x, x, x)
+    dg = runner.dims_for(w, F8 | M.MLA_FLAG_FORCE_GENERIC)
+    with pytest.raises(M.MlaError):
+        M.mla_decode_partial_balanced(dg, c, x, 4, x, x)
