@@ -204,3 +204,30 @@ def test_verify_rows_validation():
     assert call(cache=_cache(batch=20000), q_len=4) == M.MLA_ERR_UNSUPPORTED  # 80,000 rows
     assert call(q_len=0) == M.MLA_OK
     assert call(cache=_cache(batch=0)) == M.MLA_OK
+
+
+def test_fp8_flag_validation():
+    """FP8 cache rows: the quantiser's argument checks, and the flag refused where no FP8 kernel
+    exists (generic kernels forced, other shapes, the unabsorbed prefill), all before any launch."""
+    lib = M.library()
+    d = _dims()
+    assert M.MLA_FP8_ROW_BYTES == 656
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(d), None, 4, B_, None) == M.MLA_ERR_NULL
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(d), A, 4, U, None) == M.MLA_ERR_ALIGN
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(d), A, -1, B_, None) == M.MLA_ERR_SHAPE
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(_dims(d_c=256)), A, 4, B_, None) == M.MLA_ERR_UNSUPPORTED
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(_dims(dtype=M.MLA_F32)), A, 4, B_, None) == M.MLA_ERR_UNSUPPORTED
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(d), A, 0, B_, None) == M.MLA_OK
+    f8g = _dims(flags=M.MLA_FLAG_CACHE_FP8 | M.MLA_FLAG_FORCE_GENERIC)
+    f8s = _dims(flags=M.MLA_FLAG_CACHE_FP8, n_heads=64)
+    c = _cache()
+    for dd in (f8g, f8s):
+        assert _decode(dd, c) == M.MLA_ERR_UNSUPPORTED
+        assert lib.mla_decode_partial_balanced(ctypes.byref(dd), ctypes.byref(c), A, 256, B_, B_,
+                                               None) == M.MLA_ERR_UNSUPPORTED
+        assert lib.mla_prefill_chunk(ctypes.byref(dd), ctypes.byref(c), A, 4, A, B_, None,
+                                     None) == M.MLA_ERR_UNSUPPORTED
+    f8 = _dims(flags=M.MLA_FLAG_CACHE_FP8)
+    assert lib.mla_decompress_kv(ctypes.byref(f8), ctypes.byref(c), 64, A, A, B_, B_, B_, None) == M.MLA_ERR_UNSUPPORTED
+    assert lib.mla_kv_append(ctypes.byref(_dims(flags=M.MLA_FLAG_CACHE_FP8 | M.MLA_FLAG_FORCE_GENERIC)),
+                             ctypes.byref(c), 4096, A, A, A, A, A, 4, 1e-6, A, 1 << 20, None) == M.MLA_ERR_UNSUPPORTED
