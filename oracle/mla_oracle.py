@@ -366,6 +366,45 @@ def attention_loops(q_c, q_r, q_pos, cache, w_uk, w_uv, d_c, scale=None, base=10
 
 
 # --------------------------------------------------------------------------
+# Precomposed weights (offline products of consecutive projections)
+# --------------------------------------------------------------------------
+def precompose_query_weights(w_uq: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """W_absorbed[h] = W_UQ[h] . W_UK[h]^T, [H, d_cq, d_c]: the content query in latent space comes
+    straight from c^Q ([molayo] formal definition, absorbed weight; [ase] section on multiplying
+    consecutive projections ahead of time, query side)."""
+    return np.einsum("hqk,hck->hqc", np.asarray(w_uq, F64), np.asarray(w_uk, F64))
+
+
+def absorbed_query_precomposed(c_q, w_absorbed, w_qr, q_pos, base=10000.0) -> np.ndarray:
+    """q_hat_h = [c^Q . W_absorbed[h] | RoPE_pos(c^Q . W_QR[h])] for one query row c^Q [d_cq];
+    the same row as absorbed_query on q^C_h = c^Q . W_UQ[h], q^R_h = c^Q . W_QR[h]."""
+    c_q = np.asarray(c_q, F64)
+    q_lat = np.einsum("q,hqc->hc", c_q, np.asarray(w_absorbed, F64))
+    q_r = np.einsum("q,hqr->hr", c_q, np.asarray(w_qr, F64))
+    return np.concatenate([q_lat, rope(q_r, q_pos, base)], axis=-1)
+
+
+def output_projection(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """The layer output o_concat . W_O, heads concatenated: o [..., H, d_v], W_O [H * d_v, d_model]."""
+    o = np.asarray(o, F64)
+    return o.reshape(o.shape[:-2] + (-1,)) @ np.asarray(w_o, F64)
+
+
+def precompose_out_weights(w_uv: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """W~_O[h] = W_UV[h] . W_O[h], [H, d_c, d_model], with W_O[h] the d_v rows of W_O that head h's
+    output meets ([ase] section on multiplying consecutive projections ahead of time, value side;
+    [huny] section 2, value absorption and output-projection fusion)."""
+    w_uv = np.asarray(w_uv, F64)
+    H, _, d_v = w_uv.shape
+    return np.einsum("hcv,hvm->hcm", w_uv, np.asarray(w_o, F64).reshape(H, d_v, -1))
+
+
+def out_proj_fused(z: np.ndarray, w_uvo: np.ndarray) -> np.ndarray:
+    """Layer output straight from the weighted latents: sum_h z_h . W~_O[h]; z [..., H, d_c]."""
+    return np.einsum("...hc,hcm->...m", np.asarray(z, F64), np.asarray(w_uvo, F64))
+
+
+# --------------------------------------------------------------------------
 # FP8 latent cache ([huny] section 5, FP8 mixed-precision item: E4M3 on the 512-wide latent with
 # a per-token scale factor)
 # --------------------------------------------------------------------------

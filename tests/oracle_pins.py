@@ -433,10 +433,42 @@ def pin_fp8_scale_and_rows():
     assert np.array_equal(c2, codes) and np.array_equal(k2, kr) and np.array_equal(s2, scale)
 
 
+def pin_precomposed_weights():
+    """Precomposition is associativity: the precomposed query row equals the absorbed row of the
+    separately projected query (absorbed_query and query_parts are pinned on their own), and the
+    fused output equals W_O applied to the per-head outputs z . W_UV[h], including a case where a
+    selector W_O picks single head components by hand."""
+    r = _rng(51)
+    H, d_cq, d_c, d_r, d_k, d_v, d_m = 3, 5, 4, 2, 3, 2, 6
+    w_uq = r.standard_normal((H, d_cq, d_k))
+    w_uk = r.standard_normal((H, d_c, d_k))
+    w_qr = r.standard_normal((H, d_cq, d_r))
+    c_q = r.standard_normal(d_cq)
+    wa = O.precompose_query_weights(w_uq, w_uk)
+    assert wa.shape == (H, d_cq, d_c)
+    q_c = np.einsum("q,hqk->hk", c_q, w_uq)
+    q_r = np.einsum("q,hqr->hr", c_q, w_qr)
+    _close(O.absorbed_query_precomposed(c_q, wa, w_qr, 7, 1e4), O.absorbed_query(q_c, q_r, 7, w_uk, 1e4), 1e-12,
+           "precomposed query row")
+    w_uv = r.standard_normal((H, d_c, d_v))
+    w_o = r.standard_normal((H * d_v, d_m))
+    z = r.standard_normal((4, H, d_c))
+    per_head = np.einsum("rhc,hcv->rhv", z, w_uv)
+    _close(O.out_proj_fused(z, O.precompose_out_weights(w_uv, w_o)), O.output_projection(per_head, w_o), 1e-12,
+           "fused output")
+    sel = np.zeros((H * d_v, d_m))
+    sel[1 * d_v + 0, 0] = 1.0   # head 1, component 0 -> model column 0
+    sel[2 * d_v + 1, 5] = -2.0  # head 2, component 1 -> model column 5, times -2
+    fused = O.out_proj_fused(z, O.precompose_out_weights(w_uv, sel))
+    _close(fused[:, 0], per_head[:, 1, 0], 1e-12, "selector head 1")
+    _close(fused[:, 5], -2.0 * per_head[:, 2, 1], 1e-12, "selector head 2")
+    _close(fused[:, 1:5], np.zeros((4, 4)), 0.0, "selector zeros")
+
+
 ALL_PINS = {f.__name__: f for f in (
     pin_score_example, pin_key_absorption, pin_value_absorption, pin_cache_accounting,
     pin_rope_closed_forms, pin_rope_complex_form, pin_rope_relative,
     pin_sdpa_textbook, pin_sdpa_general, pin_prefill_causal, pin_loops_twin,
     pin_absorbed_equals_decompressed, pin_softmax_and_special_cases, pin_merge_partials,
-    pin_gather_rows, pin_projections, pin_fp8_e4m3, pin_fp8_scale_and_rows,
+    pin_gather_rows, pin_projections, pin_fp8_e4m3, pin_fp8_scale_and_rows, pin_precomposed_weights,
 )}

@@ -104,6 +104,12 @@ def _scale_exponent_floor(amax):
 
 
 MUTANTS = {
+    "precompose_query_untransposed_key": ("precompose_query_weights", lambda uq, uk: np.einsum(
+        "hqk,hkc->hqc", np.asarray(uq, F64), np.asarray(uk, F64).reshape(uk.shape[0], uk.shape[2], uk.shape[1]))),
+    "precompose_out_wrong_head_rows": ("precompose_out_weights", lambda uv, wo: np.einsum(
+        "hcv,hvm->hcm", np.asarray(uv, F64), np.roll(np.asarray(wo, F64).reshape(uv.shape[0], uv.shape[2], -1), 1, 0))),
+    "fused_output_drops_a_head": ("out_proj_fused", lambda z, w: np.einsum(
+        "...hc,hcm->...m", np.asarray(z, F64)[..., 1:, :], np.asarray(w, F64)[1:])),
     "e4m3_exponent_bias_8": ("e4m3_decode", _e4m3_decode_bias8),
     "e4m3_truncates": ("e4m3_encode", _e4m3_encode_truncating),
     "fp8_scale_rounds_down": ("fp8_scale_exponent", _scale_exponent_floor),
