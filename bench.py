@@ -320,6 +320,83 @@ def bench_verify(args, w) -> dict:
     }
 
 
+def bench_precomposed(args, w) -> dict:
+    """Precomposed weights on one decode step's query rows: the fused query product (c^Q . w_qcat
+    + epilogue) and the fused output product (z . W_UV W_O), each against the library's unfused
+    counterpart on the same rows (mla_absorb_query from q_C; mla_out_proj then
+    mla_output_projection).  Both fused products read their precomposed weights once per step."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import _lib as L
+    from mla_latent_kv_31_amd import runner
+    from mla_workloads import gen
+
+    dev = torch.device("cuda:0")
+    inp = gen.make_precomposed_inputs(w)
+    R, H, dq, dc, dr, dk, dv, dm = w.batch, w.n_heads, w.d_cq, w.d_c, w.d_r, w.d_k, w.d_v, w.d_model
+    d = runner.dims_for(w)
+    t = {k: runner.to_device(inp[k], dev) for k in ("w_uq", "w_qr", "w_uk", "w_uv", "w_o", "c_q", "z", "o", "pos")}
+    w_qcat = torch.empty((dq, H, dc + dr), dtype=torch.bfloat16, device=dev)
+    w_uvo = torch.empty((H, dc, dm), dtype=torch.bfloat16, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    L.mla_precompose_query(d, dq, t["w_uq"], t["w_uk"], t["w_qr"], w_qcat)
+    L.mla_precompose_out(d, dm, t["w_uv"], t["w_o"], w_uvo)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_precompose = ev0.elapsed_time(ev1)
+    wsq = L.mla_absorb_query_precomposed_workspace_bytes(d, dq, R)
+    wso = L.mla_out_proj_fused_workspace_bytes(d, dm, R)
+    wsp = L.mla_output_projection_workspace_bytes(d, dm, R)
+    ws = torch.empty(max(wsq, wso, wsp) // 4, dtype=torch.float32, device=dev)
+    q_hat = torch.empty((R, H, dc + dr), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((R, dm), dtype=torch.float32, device=dev)
+    q_c = torch.randn((R, H, dk), device=dev).to(torch.bfloat16)
+    q_r = torch.randn((R, H, dr), device=dev).to(torch.bfloat16)
+    o_h = torch.empty((R, H, dv), dtype=torch.float32, device=dev)
+    ops = {
+        "fused_query": lambda: L.mla_absorb_query_precomposed(d, dq, t["c_q"], w_qcat, t["pos"], R, q_hat, ws, wsq),
+        "fused_output": lambda: L.mla_out_proj_fused(d, dm, t["z"], w_uvo, R, out, ws, wso),
+        "absorb_query": lambda: L.mla_absorb_query(d, q_c, q_r, t["w_uk"], t["pos"], R, q_hat),
+        "out_proj": lambda: L.mla_out_proj(d, t["z"], t["w_uv"], R, o_h),
+        "output_projection": lambda: L.mla_output_projection(d, dm, t["o"], t["w_o"], R, out, ws, wsp),
+    }
+    ms = {}
+    for name, fn in ops.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms[name] = ev0.elapsed_time(ev1) / args.steps
+    ms_fused = ms["fused_query"] + ms["fused_output"]
+    ms_unfused = ms["absorb_query"] + ms["out_proj"] + ms["output_projection"]
+    bytes_fused_out = H * dc * dm * 2 + R * H * dc * 4 + R * dm * 4
+    ach = bytes_fused_out / (ms["fused_output"] * 1e-3) / 1e9
+    return {
+        "metric": "MLA precomposed-weight products, ms per decode step (V3 shape, 1 GPU)",
+        "value": round(ms_fused, 6), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_fused, 6), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rows": R, "heads": H, "d_cq": dq, "d_c": dc, "d_r": dr, "d_model": dm,
+                   "seed": w.seed},
+        "ms": {k: round(v, 6) for k, v in ms.items()},
+        "unfused_ms_per_step": round(ms_unfused, 6),
+        "unfused_note": "absorb_query starts from q_C (the c^Q . W_UQ product before it is upstream of the path)",
+        "weight_bytes": {"w_qcat": dq * H * (dc + dr) * 2, "w_uvo": H * dc * dm * 2, "w_uk": H * dc * dk * 2,
+                         "w_uv": H * dc * dv * 2, "w_o": H * dv * dm * 2},
+        "precompose_ms_once": round(ms_precompose, 3),
+        "roofline": {"bound": "hbm", "kernel": "mla_out_proj_fused", "achieved": round(ach, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "ms_per_launch": round(ms["fused_output"], 6), "algorithmic_bytes_per_launch": bytes_fused_out},
+    }
+
+
 def cpu_baseline_kv_append(inp: dict, seconds: float) -> dict:
     """The fp64 oracle's cache-write steps on rows of the same workload until `seconds` pass."""
     import oracle.mla_oracle as O
@@ -490,6 +567,9 @@ def main() -> int:
         return 0
     if w.kind == "verify":
         print(json.dumps(bench_verify(args, w)), flush=True)
+        return 0
+    if w.kind == "precomposed":
+        print(json.dumps(bench_precomposed(args, w)), flush=True)
         return 0
     if w.kind != "decode":
         print(f"workload {w.name} is not a decode, prefill, verify or cache-write workload", file=sys.stderr)

@@ -238,6 +238,43 @@ int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims);
  * non-finite values give unspecified codes (never read: slots past a sequence's length). */
 mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t rows, void* dst, void* stream);
 
+/* ---- Precomposed weights (row N2): products of consecutive projections taken once, offline
+ * ([molayo] formal definition, the absorbed weight W_UQ[h] . W_UK[h]^T; [ase] section on
+ * multiplying consecutive projections ahead of time, query and value sides; [huny] section 2,
+ * output-projection fusion).  bf16 dims with d_c 512, d_r 64 only (else MLA_ERR_UNSUPPORTED).
+ *
+ * mla_precompose_query: w_qcat[q, h, :] = [ (W_UQ[h] . W_UK[h]^T)[q, :] | W_QR[h][q, :] ], one bf16
+ * rounding of float32 sums.  w_uq bf16 [H, d_cq, d_k]; w_uk [H, d_c, d_k]; w_qr [H, d_cq, d_r];
+ * w_qcat bf16 [d_cq, H, d_c + d_r] (output).  d_cq a multiple of 64.                           */
+mla_status mla_precompose_query(const mla_dims* dims, int32_t d_cq, const void* w_uq, const void* w_uk,
+                                const void* w_qr, void* w_qcat, void* stream);
+/* mla_precompose_out: w_uvo[h] = W_UV[h] . W_O[h] with W_O[h] the d_v rows h*d_v .. of W_O.
+ * w_uv bf16 [H, d_c, d_v]; w_o bf16 [H * d_v, d_model]; w_uvo bf16 [H, d_c, d_model] (output).
+ * d_model a multiple of 128. */
+mla_status mla_precompose_out(const mla_dims* dims, int32_t d_model, const void* w_uv, const void* w_o, void* w_uvo,
+                              void* stream);
+/* The absorbed query straight from the query latent: q_hat[r, h, :] = [c_q[r] . W_absorbed[h] |
+ * RoPE_pos[r](c_q[r] . W_QR[h])] * sm_scale * log2(e), rounded to bf16 once (the layout and
+ * scaling of mla_absorb_query).  c_q bf16 [rows, d_cq]; w_qcat from mla_precompose_query; pos
+ * device int32 [rows]; q_hat bf16 [rows, H, d_c + d_r].  workspace: device float32 scratch of at
+ * least mla_absorb_query_precomposed_workspace_bytes bytes (caller-owned, overwritten). */
+size_t mla_absorb_query_precomposed_workspace_bytes(const mla_dims* dims, int32_t d_cq, int32_t rows);
+mla_status mla_absorb_query_precomposed(const mla_dims* dims, int32_t d_cq, const void* c_q, const void* w_qcat,
+                                        const int32_t* pos, int32_t rows, void* q_hat, float* workspace,
+                                        size_t workspace_bytes, void* stream);
+/* The layer output straight from the weighted latents: out[r, :] = sum_h z[r, h, :] . w_uvo[h].
+ * z float32 [rows, H, d_c] (mla_combine's output, as float32 through bf16 hi + lo parts);
+ * w_uvo from mla_precompose_out; out float32 [rows, d_model]; workspace as above. */
+size_t mla_out_proj_fused_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows);
+mla_status mla_out_proj_fused(const mla_dims* dims, int32_t d_model, const float* z, const void* w_uvo, int32_t rows,
+                              float* out, float* workspace, size_t workspace_bytes, void* stream);
+/* The unfused counterpart's last step, the output projection of the per-head outputs:
+ * out[r, :] = o[r, :, :] (heads concatenated) . W_O.  o float32 [rows, H, d_v]; w_o bf16
+ * [H * d_v, d_model]; out float32 [rows, d_model]; workspace as above. */
+size_t mla_output_projection_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows);
+mla_status mla_output_projection(const mla_dims* dims, int32_t d_model, const float* o, const void* w_o, int32_t rows,
+                                 float* out, float* workspace, size_t workspace_bytes, void* stream);
+
 /* Multi-token verify (row N4, speculative decoding) through the split-K decode path.  Query i of
  * sequence b sits at position q_start[b] + i and reads keys t <= q_start[b] + i, t < seq_lens[b]
  * (the causal rule of a chunk, [ase] causal-mask remark after Fig. 2).  Each such query is a decode

@@ -78,6 +78,14 @@ _SIGNATURES = {
     "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
     "mla_verify_rows": (_I32, [_PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_quantize_rows_fp8": (_I32, [_PD, _VP, ctypes.c_int64, _VP, _VP]),
+    "mla_precompose_query": (_I32, [_PD, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "mla_precompose_out": (_I32, [_PD, _I32, _VP, _VP, _VP, _VP]),
+    "mla_absorb_query_precomposed_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
+    "mla_absorb_query_precomposed": (_I32, [_PD, _I32, _VP, _VP, _VP, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
+    "mla_out_proj_fused_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
+    "mla_out_proj_fused": (_I32, [_PD, _I32, _VP, _VP, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
+    "mla_output_projection_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
+    "mla_output_projection": (_I32, [_PD, _I32, _VP, _VP, _I32, _VP, _VP, ctypes.c_size_t, _VP]),
 }
 
 
@@ -225,6 +233,47 @@ def mla_prefill_unabsorbed(d: MlaDims, c: MlaCache, max_len: int, q_c, q_r, q_st
 
 def mla_prefill_unabsorbed_supported(d: MlaDims) -> bool:
     return bool(library().mla_prefill_unabsorbed_supported(ctypes.byref(d)))
+
+
+def mla_precompose_query(d: MlaDims, d_cq: int, w_uq, w_uk, w_qr, w_qcat, stream=None) -> None:
+    _check(library().mla_precompose_query(ctypes.byref(d), d_cq, _addr(w_uq), _addr(w_uk), _addr(w_qr),
+                                          _addr(w_qcat), _stream(stream)), "mla_precompose_query")
+
+
+def mla_precompose_out(d: MlaDims, d_model: int, w_uv, w_o, w_uvo, stream=None) -> None:
+    _check(library().mla_precompose_out(ctypes.byref(d), d_model, _addr(w_uv), _addr(w_o), _addr(w_uvo),
+                                        _stream(stream)), "mla_precompose_out")
+
+
+def mla_absorb_query_precomposed_workspace_bytes(d: MlaDims, d_cq: int, rows: int) -> int:
+    return int(library().mla_absorb_query_precomposed_workspace_bytes(ctypes.byref(d), d_cq, rows))
+
+
+def mla_absorb_query_precomposed(d: MlaDims, d_cq: int, c_q, w_qcat, pos, rows: int, q_hat, workspace,
+                                 workspace_bytes: int, stream=None) -> None:
+    _check(library().mla_absorb_query_precomposed(ctypes.byref(d), d_cq, _addr(c_q), _addr(w_qcat), _addr(pos), rows,
+                                                  _addr(q_hat), _addr(workspace), workspace_bytes, _stream(stream)),
+           "mla_absorb_query_precomposed")
+
+
+def mla_out_proj_fused_workspace_bytes(d: MlaDims, d_model: int, rows: int) -> int:
+    return int(library().mla_out_proj_fused_workspace_bytes(ctypes.byref(d), d_model, rows))
+
+
+def mla_out_proj_fused(d: MlaDims, d_model: int, z, w_uvo, rows: int, out, workspace, workspace_bytes: int,
+                       stream=None) -> None:
+    _check(library().mla_out_proj_fused(ctypes.byref(d), d_model, _addr(z), _addr(w_uvo), rows, _addr(out),
+                                        _addr(workspace), workspace_bytes, _stream(stream)), "mla_out_proj_fused")
+
+
+def mla_output_projection_workspace_bytes(d: MlaDims, d_model: int, rows: int) -> int:
+    return int(library().mla_output_projection_workspace_bytes(ctypes.byref(d), d_model, rows))
+
+
+def mla_output_projection(d: MlaDims, d_model: int, o, w_o, rows: int, out, workspace, workspace_bytes: int,
+                          stream=None) -> None:
+    _check(library().mla_output_projection(ctypes.byref(d), d_model, _addr(o), _addr(w_o), rows, _addr(out),
+                                           _addr(workspace), workspace_bytes, _stream(stream)), "mla_output_projection")
 
 
 def mla_quantize_rows_fp8(d: MlaDims, src, rows: int, dst, stream=None) -> None:

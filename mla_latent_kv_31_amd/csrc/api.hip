@@ -349,6 +349,105 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
       launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
 }
 
+static bool precomposed_dims(const mla_dims* dims, Dims* d) {
+  return check_dims(dims, d) == MLA_OK && precomposed_supported(*d);
+}
+
+mla_status mla_precompose_query(const mla_dims* dims, int32_t d_cq, const void* w_uq, const void* w_uk,
+                                const void* w_qr, void* w_qcat, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (!precomposed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (d_cq < 64 || d_cq % 64 != 0) return MLA_ERR_SHAPE;
+  MLA_TRY(ptr_ok(w_uq));
+  MLA_TRY(ptr_ok(w_uk));
+  MLA_TRY(ptr_ok(w_qr));
+  MLA_TRY(ptr_ok(w_qcat));
+  return hip_status(launch_precompose_query(d, d_cq, w_uq, w_uk, w_qr, w_qcat, (hipStream_t)stream));
+}
+
+mla_status mla_precompose_out(const mla_dims* dims, int32_t d_model, const void* w_uv, const void* w_o, void* w_uvo,
+                              void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (!precomposed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (d_model < 128 || d_model % 128 != 0) return MLA_ERR_SHAPE;
+  if (d_model > 65536) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(w_uv));
+  MLA_TRY(ptr_ok(w_o));
+  MLA_TRY(ptr_ok(w_uvo));
+  return hip_status(launch_precompose_out(d, d_model, w_uv, w_o, w_uvo, (hipStream_t)stream));
+}
+
+size_t mla_absorb_query_precomposed_workspace_bytes(const mla_dims* dims, int32_t d_cq, int32_t rows) {
+  Dims d;
+  if (!precomposed_dims(dims, &d) || d_cq < 64 || d_cq % 64 != 0 || rows < 1) return 0;
+  return absorb_precomposed_workspace(d, d_cq, rows);
+}
+
+mla_status mla_absorb_query_precomposed(const mla_dims* dims, int32_t d_cq, const void* c_q, const void* w_qcat,
+                                        const int32_t* pos, int32_t rows, void* q_hat, float* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (!precomposed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (d_cq < 64 || d_cq % 64 != 0 || rows < 0) return MLA_ERR_SHAPE;
+  if (int64_t(rows) > 65535 * 64) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(c_q));
+  MLA_TRY(ptr_ok(w_qcat));
+  MLA_TRY(ptr_ok(pos));
+  MLA_TRY(ptr_ok(q_hat));
+  if (rows == 0) return MLA_OK;
+  MLA_TRY(ptr_ok(workspace));
+  if (workspace_bytes < absorb_precomposed_workspace(d, d_cq, rows)) return MLA_ERR_SHAPE;
+  return hip_status(launch_absorb_precomposed(d, d_cq, c_q, w_qcat, pos, rows, q_hat, workspace, (hipStream_t)stream));
+}
+
+size_t mla_out_proj_fused_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows) {
+  Dims d;
+  if (!precomposed_dims(dims, &d) || d_model < 128 || d_model % 128 != 0 || rows < 1) return 0;
+  return out_fused_workspace(d, d_model, rows);
+}
+
+mla_status mla_out_proj_fused(const mla_dims* dims, int32_t d_model, const float* z, const void* w_uvo, int32_t rows,
+                              float* out, float* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (!precomposed_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (d_model < 128 || d_model % 128 != 0 || rows < 0) return MLA_ERR_SHAPE;
+  if (d_model > 65536 || int64_t(rows) > 65535 * 64) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(z));
+  MLA_TRY(ptr_ok(w_uvo));
+  MLA_TRY(ptr_ok(out));
+  if (rows == 0) return MLA_OK;
+  MLA_TRY(ptr_ok(workspace));
+  if (workspace_bytes < out_fused_workspace(d, d_model, rows)) return MLA_ERR_SHAPE;
+  return hip_status(launch_out_fused(d, d_model, z, w_uvo, rows, out, workspace, (hipStream_t)stream));
+}
+
+size_t mla_output_projection_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t rows) {
+  Dims d;
+  if (!precomposed_dims(dims, &d) || d_model < 128 || d_model % 128 != 0 || rows < 1) return 0;
+  if ((int64_t(d.H) * d.dv) % 64 != 0) return 0;
+  return output_projection_workspace(d, d_model, rows);
+}
+
+mla_status mla_output_projection(const mla_dims* dims, int32_t d_model, const float* o, const void* w_o, int32_t rows,
+                                 float* out, float* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  MLA_TRY(check_dims(dims, &d));
+  if (!precomposed_supported(d) || (int64_t(d.H) * d.dv) % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (d_model < 128 || d_model % 128 != 0 || rows < 0) return MLA_ERR_SHAPE;
+  if (d_model > 65536 || int64_t(rows) > 65535 * 64) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(o));
+  MLA_TRY(ptr_ok(w_o));
+  MLA_TRY(ptr_ok(out));
+  if (rows == 0) return MLA_OK;
+  MLA_TRY(ptr_ok(workspace));
+  if (workspace_bytes < output_projection_workspace(d, d_model, rows)) return MLA_ERR_SHAPE;
+  return hip_status(launch_output_projection(d, d_model, o, w_o, rows, out, workspace, (hipStream_t)stream));
+}
+
 mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t rows, void* dst, void* stream) {
   Dims d;
   MLA_TRY(check_dims(dims, &d));

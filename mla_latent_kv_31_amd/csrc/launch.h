@@ -90,6 +90,22 @@ hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const vo
 // bf16 cache rows [rows, 576] -> FP8 cache rows [rows, 656 bytes] (fp8_quantize.hip).
 hipError_t launch_quantize_rows_fp8(const void* src, int64_t rows, void* dst, hipStream_t stream);
 
+// Precomposed weights (precomposed.hip).
+bool precomposed_supported(const Dims& d);
+size_t absorb_precomposed_workspace(const Dims& d, int d_cq, int rows);
+size_t out_fused_workspace(const Dims& d, int d_model, int rows);
+size_t output_projection_workspace(const Dims& d, int d_model, int rows);
+hipError_t launch_precompose_query(const Dims& d, int d_cq, const void* w_uq, const void* w_uk, const void* w_qr,
+                                   void* w_qcat, hipStream_t s);
+hipError_t launch_precompose_out(const Dims& d, int d_model, const void* w_uv, const void* w_o, void* w_uvo,
+                                 hipStream_t s);
+hipError_t launch_absorb_precomposed(const Dims& d, int d_cq, const void* c_q, const void* w_qcat, const int32_t* pos,
+                                     int rows, void* q_hat, float* workspace, hipStream_t s);
+hipError_t launch_out_fused(const Dims& d, int d_model, const float* z, const void* w_uvo, int rows, float* out,
+                            float* workspace, hipStream_t s);
+hipError_t launch_output_projection(const Dims& d, int d_model, const float* o, const void* w_o, int rows, float* out,
+                                    float* workspace, hipStream_t s);
+
 // Multi-token verify rows for the decode path (verify_rows.hip).
 hipError_t launch_verify_rows(const Cache& c, const int32_t* q_start, int q_len, int32_t* row_table,
                               int32_t* row_lens, int32_t* row_pos, hipStream_t stream);

@@ -56,6 +56,7 @@ class Workload:
     name: str
     seed: int
     kind: str                       # "toy" | "decode" | "prefill" | "kv_append" | "verify" (prefill inputs)
+    #                                 | "precomposed"
     batch: int
     n_heads: int = 128
     d_c: int = 512
@@ -110,6 +111,11 @@ WORKLOADS: dict[str, Workload] = {
         name="v3_kv_append_prefill_b2", seed=7, kind="kv_append", batch=2, ctx=2048, q_len=512,
         random_pages=True, d_model=4096,
         notes="the 512-token chunk of each of 2 sequences, written at positions 2048..2559"),
+    # precomposed weights: the query side from the query latent and the fused output projection,
+    # d_cq 1536 and d_model 4096 as in the [molayo] implementation code
+    "v3_precomposed_b64": Workload(
+        name="v3_precomposed_b64", seed=9, kind="precomposed", batch=64, q_len=1, d_model=4096, d_cq=1536,
+        notes="64 query rows (one decode step of the ragged batch): c^Q [64, 1536], z [64, 128, 512]"),
     # multi-token verify (speculative decoding): 4 draft tokens per sequence of the ragged batch
     "v3_verify_b64_sq4": Workload(
         name="v3_verify_b64_sq4", seed=8, kind="verify", batch=64, ctx_range=(1024, 32768), q_len=4,
@@ -119,7 +125,7 @@ WORKLOADS: dict[str, Workload] = {
 }
 
 WORKLOAD_ORDER = ["toy_fp32", "v3_b1_ctx4k", "v3_b64_ragged_paged", "v3_b4_ctx128k", "v3_prefill_b2",
-                  "v3_kv_append_b64", "v3_kv_append_prefill_b2", "v3_verify_b64_sq4"]
+                  "v3_kv_append_b64", "v3_kv_append_prefill_b2", "v3_verify_b64_sq4", "v3_precomposed_b64"]
 
 
 # --------------------------------------------------------------------------
@@ -271,6 +277,30 @@ def make_prefill_inputs(w: Workload, *, seed: int | None = None, fill: str = "ra
                 q_c=_store(q_c, w.dtype), q_r=_store(q_r, w.dtype),
                 w_uk=_store(w_uk, w.dtype), w_uv=_store(w_uv, w.dtype),
                 pool=pool, page_table=table)
+
+
+def make_precomposed_inputs(w: Workload, *, rows: int | None = None, seed: int | None = None) -> dict:
+    """Inputs of the precomposed-weight products for `rows` query rows.
+
+    Draw order: W_UQ, W_QR, W_UK, W_UV, W_O, c^Q, z, o, positions.  Weights are N(0,1)/sqrt(fan-in)
+    (d_cq for W_UQ and W_QR, d_c for W_UK and W_UV, H * d_v for W_O) stored bf16; c^Q is N(0,1)
+    bf16; the weighted latents z and the per-head outputs o are N(0,1) float32; positions are
+    uniform on [0, 131072).
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    R = w.batch if rows is None else rows
+    H, dc, dr, dk, dv, dq, dm = w.n_heads, w.d_c, w.d_r, w.d_k, w.d_v, w.d_cq, w.d_model
+    out = dict(workload=w, dtype=w.dtype, rows=R)
+    out["w_uq"] = _store(_normal(rng, (H, dq, dk), 1.0 / math.sqrt(dq)), w.dtype)
+    out["w_qr"] = _store(_normal(rng, (H, dq, dr), 1.0 / math.sqrt(dq)), w.dtype)
+    out["w_uk"] = _store(_normal(rng, (H, dc, dk), 1.0 / math.sqrt(dc)), w.dtype)
+    out["w_uv"] = _store(_normal(rng, (H, dc, dv), 1.0 / math.sqrt(dc)), w.dtype)
+    out["w_o"] = _store(_normal(rng, (H * dv, dm), 1.0 / math.sqrt(H * dv)), w.dtype)
+    out["c_q"] = _store(_normal(rng, (R, dq)), w.dtype)
+    out["z"] = _normal(rng, (R, H, dc)).astype(np.float32)
+    out["o"] = _normal(rng, (R, H, dv)).astype(np.float32)
+    out["pos"] = rng.integers(0, 131072, size=R, dtype=np.int64).astype(np.int32)
+    return out
 
 
 def make_toy_inputs(w: Workload | None = None, *, seed: int | None = None) -> dict:

@@ -372,15 +372,15 @@ def precompose_query_weights(w_uq: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
     """W_absorbed[h] = W_UQ[h] . W_UK[h]^T, [H, d_cq, d_c]: the content query in latent space comes
     straight from c^Q ([molayo] formal definition, absorbed weight; [ase] section on multiplying
     consecutive projections ahead of time, query side)."""
-    return np.einsum("hqk,hck->hqc", np.asarray(w_uq, F64), np.asarray(w_uk, F64))
+    return np.matmul(np.asarray(w_uq, F64), np.swapaxes(np.asarray(w_uk, F64), 1, 2))
 
 
 def absorbed_query_precomposed(c_q, w_absorbed, w_qr, q_pos, base=10000.0) -> np.ndarray:
     """q_hat_h = [c^Q . W_absorbed[h] | RoPE_pos(c^Q . W_QR[h])] for one query row c^Q [d_cq];
     the same row as absorbed_query on q^C_h = c^Q . W_UQ[h], q^R_h = c^Q . W_QR[h]."""
     c_q = np.asarray(c_q, F64)
-    q_lat = np.einsum("q,hqc->hc", c_q, np.asarray(w_absorbed, F64))
-    q_r = np.einsum("q,hqr->hr", c_q, np.asarray(w_qr, F64))
+    q_lat = np.tensordot(c_q, np.asarray(w_absorbed, F64), axes=([0], [1]))   # [H, d_c]
+    q_r = np.tensordot(c_q, np.asarray(w_qr, F64), axes=([0], [1]))           # [H, d_r]
     return np.concatenate([q_lat, rope(q_r, q_pos, base)], axis=-1)
 
 
@@ -396,12 +396,14 @@ def precompose_out_weights(w_uv: np.ndarray, w_o: np.ndarray) -> np.ndarray:
     [huny] section 2, value absorption and output-projection fusion)."""
     w_uv = np.asarray(w_uv, F64)
     H, _, d_v = w_uv.shape
-    return np.einsum("hcv,hvm->hcm", w_uv, np.asarray(w_o, F64).reshape(H, d_v, -1))
+    return np.matmul(w_uv, np.asarray(w_o, F64).reshape(H, d_v, -1))
 
 
 def out_proj_fused(z: np.ndarray, w_uvo: np.ndarray) -> np.ndarray:
     """Layer output straight from the weighted latents: sum_h z_h . W~_O[h]; z [..., H, d_c]."""
-    return np.einsum("...hc,hcm->...m", np.asarray(z, F64), np.asarray(w_uvo, F64))
+    z = np.asarray(z, F64)
+    w_uvo = np.asarray(w_uvo, F64)
+    return z.reshape(z.shape[:-2] + (-1,)) @ w_uvo.reshape(-1, w_uvo.shape[-1])
 
 
 # --------------------------------------------------------------------------
