@@ -245,3 +245,32 @@ def test_fp8_unsupported_paths():
     dg = runner.dims_for(w, F8 | M.MLA_FLAG_FORCE_GENERIC)
     with pytest.raises(M.MlaError):
         M.mla_decode_partial_balanced(dg, c, x, 4, x, x)
+
+
+@pytest.mark.parametrize("mode", ["fixed_8192", "balanced_2"])
+def test_fp8_decode_long_segments(mode):
+    """Segments longer than 64 pages, so the kernel moves its page window inside a segment (the
+    rotary rows of the next tile keep the address taken before the move): one 10,000-token and one
+    5,000-token sequence, fixed 8,192-token chunks or two balanced units.  Bitwise against the bf16
+    decode of the dequantised pool, and against the oracle on three heads."""
+    w = gen.Workload(name="fp8_long", seed=76, kind="decode", batch=2, ctx_range=(1, 10000), random_pages=True)
+    inp = gen.make_decode_inputs(w, lens=np.array([10000, 5000], np.int32))
+    pool8 = oracle_fp8_pool(inp["pool"])
+    inp8 = dict(inp, pool=pool8)
+    inpb = dict(inp, pool=dequantized_bf16_pool(pool8))
+    kw = dict(split_tokens=8192) if mode == "fixed_8192" else dict(n_units=2)
+    note(f"fp8 decode long segments {mode}")
+    st8 = runner.DecodeStep(inp8, device=DEV, flags=F8, **kw)
+    stb = runner.DecodeStep(inpb, device=DEV, **kw)
+    st8.run()
+    stb.run()
+    torch.cuda.synchronize()
+    for name in ("z", "lse", "out"):
+        a, b = getattr(st8, name).cpu().numpy(), getattr(stb, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{name}: FP8 and bf16-of-FP8 differ"
+    view = Fp8View(inp8, pool8)
+    tol = TOL["bf16"]
+    for b in range(2):
+        ref = view.decode(b, heads=HEADS)
+        assert_abs_close(_np(st8.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
+        assert_rms_close(_np(st8.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
