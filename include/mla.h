@@ -234,7 +234,8 @@ int32_t mla_prefill_unabsorbed_supported(const mla_dims* dims);
 
 /* bf16 cache rows -> FP8 cache rows (MLA_FLAG_CACHE_FP8 layout), row by row; the scale of each row
  * comes from its own 512 latent values.  src device bf16 [rows, 576]; dst device bytes
- * [rows, MLA_FP8_ROW_BYTES].  Only d_c 512, d_r 64 in bf16 (else MLA_ERR_UNSUPPORTED).  Rows holding
+ * [rows, MLA_FP8_ROW_BYTES].  Only d_c 512, d_r 64 in bf16, at most 4 * (2^31 - 1) rows (else
+ * MLA_ERR_UNSUPPORTED).  Rows holding
  * non-finite values give unspecified codes (never read: slots past a sequence's length). */
 mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t rows, void* dst, void* stream);
 

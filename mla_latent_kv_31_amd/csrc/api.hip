@@ -453,7 +453,7 @@ mla_status mla_quantize_rows_fp8(const mla_dims* dims, const void* src, int64_t 
   MLA_TRY(check_dims(dims, &d));
   if (d.dtype != MLA_BF16 || d.dc != 512 || d.dr != 64) return MLA_ERR_UNSUPPORTED;
   if (rows < 0) return MLA_ERR_SHAPE;
-  if (rows > (int64_t(1) << 33)) return MLA_ERR_UNSUPPORTED;
+  if (rows > int64_t(4) * 0x7fffffff) return MLA_ERR_UNSUPPORTED;  // four rows per workgroup, 2^31 - 1 workgroups
   MLA_TRY(ptr_ok(src));
   MLA_TRY(ptr_ok(dst));
   if (rows == 0) return MLA_OK;

@@ -218,6 +218,7 @@ def test_fp8_flag_validation():
     assert lib.mla_quantize_rows_fp8(ctypes.byref(_dims(d_c=256)), A, 4, B_, None) == M.MLA_ERR_UNSUPPORTED
     assert lib.mla_quantize_rows_fp8(ctypes.byref(_dims(dtype=M.MLA_F32)), A, 4, B_, None) == M.MLA_ERR_UNSUPPORTED
     assert lib.mla_quantize_rows_fp8(ctypes.byref(d), A, 0, B_, None) == M.MLA_OK
+    assert lib.mla_quantize_rows_fp8(ctypes.byref(d), A, 4 * 0x7FFFFFFF + 1, B_, None) == M.MLA_ERR_UNSUPPORTED
     f8g = _dims(flags=M.MLA_FLAG_CACHE_FP8 | M.MLA_FLAG_FORCE_GENERIC)
     f8s = _dims(flags=M.MLA_FLAG_CACHE_FP8, n_heads=64)
     c = _cache()
