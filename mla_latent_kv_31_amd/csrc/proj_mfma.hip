@@ -62,7 +62,7 @@ struct RopeFreq {
   double v[kMaxDr / 2];
 };
 
-template <int RB>
+template <int RB, int CS>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, RopeFreq inv_freq, float qscale,
                                                           const uint16_t* __restrict__ q_c,
                                                           const uint16_t* __restrict__ q_r,
@@ -70,9 +70,13 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
                                                           const int32_t* __restrict__ pos, uint16_t* __restrict__ q_hat) {
   __shared__ __attribute__((aligned(16))) unsigned char ab_smem[32 * RB * (kDc + kMaxDr + 8) * 2];
   constexpr int kRows = 32 * RB;
+  constexpr int kJB = 4 / CS;             // 32-column blocks per wave
+  constexpr int kPartCols = kDc / CS;     // latent columns per workgroup
   const int slices = (R + kRows - 1) / kRows;
-  int h, rs;
-  if (!xcd_head_map(slices, H, h, rs)) return;
+  int h, inner;
+  if (!xcd_head_map(slices * CS, H, h, inner)) return;
+  const int rs = inner / CS, part = inner % CS;
+  const bool do_rope = part == 0;         // the first column part also rotates q_R (uniform)
   const int r0 = kRows * rs, nrows = min(kRows, R - r0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5;
   const int W = kDc + dr;
@@ -100,25 +104,26 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
   for (int t = 0; t < RB; ++t) {
     const int idx = threadIdx.x + 256 * t, rr = idx / max(quads, 1), qd = idx - rr * max(quads, 1);
-    const bool ok = idx < nrows * quads;
+    const bool ok = do_rope && idx < nrows * quads;
     const int r = ok ? r0 + rr : r0;
     rin[t] = ok ? *reinterpret_cast<const u32x4*>(q_r + (size_t(r) * H + h) * dr + 8 * qd) : u32x4{0u, 0u, 0u, 0u};
     rpos[t] = ok ? pos[r] : 0;
   }
   double fr = 0.0;  // the frequency table entry this thread stages in LDS
   if (threadIdx.x < kMaxDr / 2) fr = inv_freq.v[threadIdx.x];
-  // A operands of all four column blocks, loaded together with the B operands so that the wave
-  // waits for memory once
-  const uint16_t* wbase = w_uk + (size_t(h) * kDc + 128 * wave + (lane & 31)) * kDk + 8 * hi;
-  bf16x8 a[4][kDk / 16];
+  // A operands of this wave's column blocks (latent columns col0 .. col0 + 32 kJB), loaded together
+  // with the B operands so that the wave waits for memory once
+  const int col0 = kPartCols * part + 32 * kJB * wave;
+  const uint16_t* wbase = w_uk + (size_t(h) * kDc + col0 + (lane & 31)) * kDk + 8 * hi;
+  bf16x8 a[kJB][kDk / 16];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+  for (int jb = 0; jb < kJB; ++jb)
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) a[jb][ks] = load_bf16x8(wbase + size_t(32 * jb) * kDk + 16 * ks);
   // an empty asm that reads every loaded value: the compiler would otherwise move loads next to
   // their uses and put several memory latencies in a row on the critical path
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+  for (int jb = 0; jb < kJB; ++jb)
 #pragma unroll
     for (int ks = 0; ks < kDk / 16; ++ks) asm volatile("" : "+v"(a[jb][ks]));
 #pragma unroll
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
     asm volatile("" : "+v"(rin[rb]), "+v"(rpos[rb]));
   }
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
+  for (int jb = 0; jb < kJB; ++jb) {
     f32x16 acc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -139,10 +144,10 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jb][ks], bq[rb][ks], acc[rb], 0, 0, 0);
-    // D layout: lane holds row 32rb + lane%32 and columns j = 128w + 32jb + 8g + 4hi + 0..3
+    // D layout: lane holds row 32rb + lane%32 and columns j = col0 + 32jb + 8g + 4hi + 0..3
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      lds_u16* trow = tile + (32 * rb + (lane & 31)) * TW + 128 * wave + 32 * jb + 4 * hi;
+      lds_u16* trow = tile + (32 * rb + (lane & 31)) * TW + col0 + 32 * jb + 4 * hi;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 v;
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
   for (int t = 0; t < RB; ++t) {
     const int idx = threadIdx.x + 256 * t;
-    if (idx >= nrows * quads) break;
+    if (!do_rope || idx >= nrows * quads) break;
     const int rr = idx / quads, qd = idx - rr * quads;
     const u32x4 in = rin[t];
     const double p = double(rpos[t]);
@@ -180,10 +185,12 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
     *(lds_u32x4*)(tile + rr * TW + kDc + 8 * qd) = outv;
   }
   __syncthreads();
-  // write the tile: row rr of the workgroup is q_hat[(r0 + rr) * H + h][0 .. W)
-  const int chunks = W / 8;
+  // write the tile: row rr of the workgroup is q_hat[(r0 + rr) * H + h], this part's latent columns
+  // and (first part) the rotary columns
+  const int lat_chunks = kPartCols / 8, chunks = lat_chunks + (do_rope ? dr / 8 : 0);
   for (int idx = threadIdx.x; idx < nrows * chunks; idx += blockDim.x) {
-    const int rr = idx / chunks, c = idx % chunks;
+    const int rr = idx / chunks, cc = idx % chunks;
+    const int c = cc < lat_chunks ? kPartCols / 8 * part + cc : kDc / 8 + (cc - lat_chunks);
     const u32x4 v = *(const lds_u32x4*)(tile + rr * TW + 8 * c);
     *reinterpret_cast<u32x4*>(q_hat + (size_t(r0 + rr) * H + h) * W + 8 * c) = v;
   }
@@ -446,11 +453,11 @@ hipError_t launch_absorb_mfma(const Dims& d, const void* q_c, const void* q_r, c
   const uint16_t* wk = static_cast<const uint16_t*>(w_uk);
   RopeFreq inv{};
   for (int i = 0; i < d.dr / 2; ++i) inv.v[i] = pow(double(d.rope_base), -2.0 * i / d.dr);
-  if (rows <= 4 * 32)  // small batch: 32-row workgroups
-    absorb_mfma_kernel<1><<<dim3(xcd_grid((rows + 31) / 32, d.H)), 256, 0, s>>>(
+  if (rows <= 4 * 32)  // small batch: 32-row workgroups, the latent columns split in two halves
+    absorb_mfma_kernel<1, 2><<<dim3(xcd_grid(2 * ((rows + 31) / 32), d.H)), 256, 0, s>>>(
         d.H, rows, d.dr, inv, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
   else
-    absorb_mfma_kernel<2><<<dim3(xcd_grid((rows + 63) / 64, d.H)), 256, 0, s>>>(
+    absorb_mfma_kernel<2, 1><<<dim3(xcd_grid((rows + 63) / 64, d.H)), 256, 0, s>>>(
         d.H, rows, d.dr, inv, qscale, qc, qr, wk, pos, static_cast<uint16_t*>(q_hat));
   return hipGetLastError();
 }
