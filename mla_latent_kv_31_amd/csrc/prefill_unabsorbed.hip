@@ -94,6 +94,19 @@ constexpr int kDcLds = kDcOutB > kDcBuf * kDcChunkB ? kDcOutB : kDcBuf * kDcChun
 // f(r) = ((r & 3) << 2) | ((r >> 2) & 3): 16 consecutive rows at one logical chunk (row-wise reads)
 // and 4 rows x 4 chunks (transposing reads) hit 16 distinct bank groups.  128-byte k^R rows: chunk
 // c of row r at c ^ ((r >> 1) & 7).
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  The per_group
+// workgroups of group grp all run on XCD grp % 8 (linear id 8k + grp % 8), so the data they share
+// (a head's weights, a sequence-head's keys and values) is fetched from HBM once, not once per XCD.
+__device__ __forceinline__ bool xcd_group_map(int per_group, int groups, int& grp, int& inner) {
+  const int id = blockIdx.x, k = id >> 3;
+  grp = (k / per_group) * 8 + (id & 7);
+  inner = k % per_group;
+  return grp < groups;
+}
+__host__ inline unsigned xcd_group_grid(int per_group, int groups) {
+  return unsigned(8 * ((groups + 7) / 8) * per_group);
+}
+
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int kr_swz(int r) { return (r >> 1) & 7; }
 
@@ -104,7 +117,11 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
                                                                uint16_t* __restrict__ kr_out) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kDcLds];
   lds_u8* const lbase = (lds_u8*)smem;
-  const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // group = head (its W_UK and W_UV slices), members = (sequence, 128-token block)
+  const int ntb = (max_len + kDcTok - 1) / kDcTok;
+  int h, inner;
+  if (!xcd_group_map(ntb * c.batch, kH, h, inner)) return;
+  const int tb = inner % ntb, b = inner / ntb;
   const int len = min(c.seq_lens[b], c.max_pages * c.page_size);
   const int t0 = tb * kDcTok;
   if (t0 >= len) return;  // uniform
@@ -138,10 +155,10 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
 #pragma unroll
     for (int u = 0; u < 2; ++u) dma16_at(dst + uint32_t(kDcWB + (2 * wv + u) * 1024), crow[u] + kDcJ * k);
   };
-  // B operand: latents of token 32*wave + lane%32 at j = 16s + 8hi of the chunk (64-byte token rows,
+  // B operand: latents of token 32*tb + lane%32 at j = 16s + 8hi of the chunk (64-byte token rows,
   // chunk c of row r at c ^ ((r >> 2) & 3))
-  auto b_op = [&](int buf, int s) {
-    const int r = 32 * wave + (lane & 31);
+  auto b_op = [&](int buf, int s, int tb) {
+    const int r = 32 * tb + (lane & 31);
     return lds16(lbase + buf * kDcChunkB + kDcWB + r * 64 + 16 * ((2 * s + hi) ^ ((r >> 2) & 3)));
   };
   // A operand of output block ob (0..3: K columns 32ob.., 4..7: V) at k-step s of a chunk: group g
@@ -156,11 +173,13 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
     return tr_pair(p0, p1);
   };
 
-  f32x16 acc[8];
+  // wave w owns output blocks 2w and 2w+1 (K columns for w < 2, V columns beyond) for all four
+  // 32-token blocks: each weight operand read from LDS feeds four MFMAs, each latent operand two
+  f32x16 acc[8];  // [2 * 0 + tb] and [4 + tb]: blocks 2w and 2w+1 of token block tb
 #pragma unroll
-  for (int ob = 0; ob < 8; ++ob)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[ob][x] = 0.f;
+    for (int x = 0; x < 16; ++x) acc[a][x] = 0.f;
 
   // chunks k and k+1 in flight while chunk k is multiplied; every iteration issues the same
   // transfers (past the end they repeat the last chunk into the free buffer), so one wait count
@@ -174,30 +193,38 @@ __global__ __launch_bounds__(256, 2) void decompress_kv_kernel(Cache c, int max_
     const int buf = k % kDcBuf;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 bq = b_op(buf, s);
+      bf16x8 bq[4];
 #pragma unroll
-      for (int ob = 0; ob < 8; ++ob)
-        acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op(buf, s, ob), bq, acc[ob], 0, 0, 0);
+      for (int tb = 0; tb < 4; ++tb) bq[tb] = b_op(buf, s, tb);
+#pragma unroll
+      for (int obl = 0; obl < 2; ++obl) {
+        const bf16x8 aw = a_op(buf, s, 2 * wave + obl);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[4 * obl + tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bq[tb], acc[4 * obl + tb], 0, 0, 0);
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // every wave is done with the chunk buffers and no transfer is in flight
 
-  // D layout: lane holds token lane%32 of the wave and columns 32ob + 8(x/4) + 4hi + x%4.  Stage
+  // D layout: lane holds token 32tb + lane%32 and columns 32ob + 8(x/4) + 4hi + x%4.  Stage
   // [128 tokens][K row | V row] in LDS, then write whole rows.
-  {
-    lds_u8* const orow = lbase + (32 * wave + (lane & 31)) * kDcOutRow;
 #pragma unroll
-    for (int ob = 0; ob < 8; ++ob)
+  for (int obl = 0; obl < 2; ++obl)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      lds_u8* const orow = lbase + (32 * tb + (lane & 31)) * kDcOutRow;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = 32 * ob + 8 * q + 4 * hi;  // 0..255 across K | V
+        const int col = 32 * (2 * wave + obl) + 8 * q + 4 * hi;  // 0..255 across K | V
+        const f32x16& a = acc[4 * obl + tb];
         u32x2 v;
-        v[0] = f16_bits(acc[ob][4 * q]) | (f16_bits(acc[ob][4 * q + 1]) << 16);
-        v[1] = f16_bits(acc[ob][4 * q + 2]) | (f16_bits(acc[ob][4 * q + 3]) << 16);
+        v[0] = f16_bits(a[4 * q]) | (f16_bits(a[4 * q + 1]) << 16);
+        v[1] = f16_bits(a[4 * q + 2]) | (f16_bits(a[4 * q + 3]) << 16);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(orow + 2 * col) = v;
       }
-  }
+    }
   __syncthreads();
   const int ntok = min(kDcTok, len - t0);
   const size_t obase = (size_t(b) * kH + h) * max_len + t0;
@@ -238,13 +265,16 @@ struct RopeTab {
 };
 
 __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
-    const int32_t* __restrict__ seq_lens, int cap, int max_len, const uint16_t* __restrict__ q_c,
+    int batch, const int32_t* __restrict__ seq_lens, int cap, int max_len, const uint16_t* __restrict__ q_c,
     const uint16_t* __restrict__ q_r, const int32_t* __restrict__ q_start, int q_len, float qscale, RopeTab rope,
     const uint16_t* __restrict__ k_in, const uint16_t* __restrict__ v_in, const uint16_t* __restrict__ kr_in,
     float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kAtBuf * kTileB];  // 80 KiB
   lds_u8* const lbase = (lds_u8*)smem;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // group = (sequence, head) (its keys and values), members = 128-query blocks
+  int grp, qb;
+  if (!xcd_group_map((q_len + kAtQ - 1) / kAtQ, batch * kH, grp, qb)) return;
+  const int h = grp % kH, b = grp / kH;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
   const int len = min(seq_lens[b], cap);
   const int qs = q_start[b];
@@ -443,8 +473,8 @@ bool prefill_unabsorbed_supported(const Dims& d) {
 hipError_t launch_decompress_kv(const Dims& d, const Cache& c, int max_len, const void* w_uk, const void* w_uv,
                                 void* k_out, void* v_out, void* kr_out, hipStream_t s) {
   (void)d;
-  const dim3 grid((max_len + kDcTok - 1) / kDcTok, kH, c.batch);
-  decompress_kv_kernel<<<grid, 256, 0, s>>>(c, max_len, static_cast<const uint16_t*>(w_uk),
+  const int ntb = (max_len + kDcTok - 1) / kDcTok;
+  decompress_kv_kernel<<<dim3(xcd_group_grid(ntb * c.batch, kH)), 256, 0, s>>>(c, max_len, static_cast<const uint16_t*>(w_uk),
                                             static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(k_out),
                                             static_cast<uint16_t*>(v_out), static_cast<uint16_t*>(kr_out));
   return hipGetLastError();
@@ -456,8 +486,8 @@ hipError_t launch_attend_unabsorbed(const Dims& d, const Cache& c, int max_len, 
   RopeTab rope;
   for (int i = 0; i < kDr / 2; ++i) rope.v[i] = pow(double(d.rope_base), -2.0 * i / kDr);
   const float qscale = d.sm_scale * kLog2e;
-  const dim3 grid((q_len + kAtQ - 1) / kAtQ, kH, c.batch);
-  attend_unabsorbed_kernel<<<grid, 256, 0, s>>>(c.seq_lens, c.max_pages * c.page_size, max_len,
+  const dim3 grid(xcd_group_grid((q_len + kAtQ - 1) / kAtQ, c.batch * kH));
+  attend_unabsorbed_kernel<<<grid, 256, 0, s>>>(c.batch, c.seq_lens, c.max_pages * c.page_size, max_len,
                                                 static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(q_r),
                                                 q_start, q_len, qscale, rope, static_cast<const uint16_t*>(k),
                                                 static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(kr), out,
