@@ -276,8 +276,11 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
   if (!xcd_group_map((q_len + kAtQ - 1) / kAtQ, batch * kH, grp, qb)) return;
   const int h = grp % kH, b = grp / kH;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
-  const int len = min(seq_lens[b], cap);
-  const int qs = q_start[b];
+  // workgroup- and wave-uniform values kept in scalar registers, so that the tile loop and its
+  // per-tile decisions stay scalar branches instead of masked vector code
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int len = __builtin_amdgcn_readfirstlane(min(seq_lens[b], cap));
+  const int qs = __builtin_amdgcn_readfirstlane(q_start[b]);
   const int q0 = kAtQ * qb;  // first query of the workgroup (chunk index)
   if (q0 >= q_len) return;
   const int qi = q0 + 32 * wave + (lane & 31);  // this lane's query (chunk index)
@@ -370,7 +373,6 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[db][x] = 0.f;
   float m_run = -INFINITY, l_lane = 0.f;
-  const int wq_last = qs + min(q0 + 32 * wave + 31, q_len - 1);  // the wave's last query position
 
   // tiles 0..2 in flight before the loop; past the last tile the transfers repeat it (into a
   // buffer nobody reads), which keeps every wait count uniform
@@ -386,7 +388,10 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
     dma_tile(min(j + kAtBuf - 1, ntiles - 1), (j + kAtBuf - 1) % kAtBuf);
     const lds_u8* const tb = lbase + (j % kAtBuf) * kTileB;
     const int tt0 = kAtT * j;
-    if (tt0 <= wq_last) {  // the wave sees some token of this tile (uniform)
+    // Every wave scores every tile: tiles past a wave's last query are fully masked (weight 0).
+    // Skipping them behind a branch made the compiler copy the accumulators and the softmax
+    // state at every loop edge, which cost more than the few masked tiles of the diagonal block.
+    {
       f32x16 s;
 #pragma unroll
       for (int x = 0; x < 16; ++x) s[x] = 0.f;
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
 #pragma unroll
       for (int x = 0; x < 16; ++x) s[x] *= qscale;  // base-2 logits
       // mask: tokens past the query's position or the sequence end
-      if (tt0 + kAtT - 1 > qs + q0 + 32 * wave || tt0 + kAtT > len) {
+      if (tt0 + kAtT - 1 > qs + q0 + 32 * wv || tt0 + kAtT > len) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int t = tt0 + 8 * (x >> 2) + 4 * hi + (x & 3);
@@ -409,17 +414,17 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
       }
+      // rescale the running sums by exp2(old max - new max), branch-free (factor 1 where the
+      // maximum stayed, -inf included when no key is visible yet): a conditional rescale made the
+      // compiler copy the accumulators around the branch every tile
       const float m_new = fmaxf(m_run, mx);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {  // some maximum moved: rescale
-        // (lanes whose maximum stayed, -inf included when no key is visible yet, keep factor 1)
-        const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
-        l_lane *= alpha;
+      const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+      l_lane *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
-        m_run = m_new;
-      }
+        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+      m_run = m_new;
       // probabilities times 2^kPShift (at most 2^15, inside binary16), so that weights far below
       // the maximum stay normal numbers; the factor cancels in out and is taken off lse
       float p[16], tsum = 0.f;
