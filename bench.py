@@ -79,6 +79,38 @@ def _blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_copy_gbs(dev, mib: int = 1024, reps: int = 20) -> float:
+    """HBM bandwidth of a plain device-to-device copy (bytes read + bytes written per second),
+    the achievable denominator beside the published peak; the buffers exceed the 256 MB
+    Infinity Cache several times over."""
+    import torch
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * (mib << 20) / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(inp: dict, seconds: float) -> dict:
     """The fp64 oracle, as it stands, on whole sequences of the same workload until `seconds` pass."""
     import numpy as np
@@ -104,7 +136,7 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
     el = time.perf_counter() - t0
     row_bytes = (w.d_c + w.d_r) * (2 if dt == "bf16" else 4)
     return {"value": round(toks * row_bytes / el / 1e9, 6), "unit": "GB/s", "cores": _blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"first {n} of {w.batch} sequences ({toks} cached tokens, all {w.n_heads} heads, "
                       f"unabsorbed fp64 NumPy) in {el:.1f} s"}
 
@@ -132,6 +164,7 @@ def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
             break
     el = time.perf_counter() - t0
     return {"value": round(flops / el / 1e12, 9), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"first {n} of {w.q_len} query rows of sequence 0 (all {w.n_heads} heads, unabsorbed fp64 "
                       f"NumPy; algorithmic absorbed flops counted) in {el:.1f} s"}
 
@@ -417,6 +450,7 @@ def cpu_baseline_kv_append(inp: dict, seconds: float) -> dict:
     el = time.perf_counter() - t0
     nbytes = _kv_append_bytes(w, n)
     return {"value": round(nbytes / el / 1e9, 6), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"first {n} of {inp['h'].shape[0]} new rows (fp64 NumPy; algorithmic bytes counted) "
                       f"in {el:.1f} s"}
 
@@ -627,7 +661,9 @@ def main() -> int:
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    ms_decode = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_decode = float(np.mean(launch_ms))
+    copy_gbs = measured_copy_gbs(dev)  # outside the timed region
 
     sha = _kernel_sha()
     traffic = None if args.fp8 else _traffic(w.name, sha)
@@ -658,7 +694,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "mla_decode_partial", "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_decode, 6),
-                     "algorithmic_bytes_per_launch": cache_bytes, "kernel_source_sha": sha},
+                     "ms_per_launch_median": round(float(np.median(launch_ms)), 6),
+                     "algorithmic_bytes_per_launch": cache_bytes, "kernel_source_sha": sha,
+                     "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
         "roofline_mfma": {"achieved": round(flops_decode / (ms_decode * 1e-3) / 1e12, 3),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(flops_decode / (ms_decode * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
