@@ -664,6 +664,17 @@ def main() -> int:
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_decode = float(np.mean(launch_ms))
     copy_gbs = measured_copy_gbs(dev)  # outside the timed region
+    # the same step captured once in a HIP graph and replayed: one host launch per step
+    graph = runner.CapturedStep(st)
+    for _ in range(max(args.warmup // 4, 1)):
+        graph.run()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        graph.run()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
 
     sha = _kernel_sha()
     traffic = None if args.fp8 else _traffic(w.name, sha)
@@ -691,6 +702,9 @@ def main() -> int:
         "cache_tokens_per_s": round(total_tokens / (ms_step * 1e-3), 1),
         "tflops": round((flops_decode + flops_proj) / (ms_step * 1e-3) / 1e12, 3),
         "wall_s": round(t_wall, 4),
+        "graph": {"ms_per_step": round(ms_graph, 6), "value": round(cache_bytes / (ms_graph * 1e-3) / 1e9, 3),
+                  "tokens_per_s": round(w.batch / (ms_graph * 1e-3), 1),
+                  "note": "the same four launches captured in one HIP graph and replayed K times"},
         "roofline": {"bound": "hbm", "kernel": "mla_decode_partial", "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_decode, 6),

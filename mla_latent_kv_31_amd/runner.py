@@ -12,6 +12,7 @@ Chunked prefill (q_len query tokens per sequence):
 Multi-token verify (q_len query tokens per sequence, as batch * q_len decode rows):
     mla_verify_rows -> mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced
     -> mla_out_proj
+Any of these sequences can be captured once in a HIP graph and replayed (CapturedStep).
 """
 
 from __future__ import annotations
@@ -281,3 +282,31 @@ class PrefillUnabsorbedStep:
     def run(self, stream=None):
         self.decompress(stream)
         self.attend(stream)
+
+
+class CapturedStep:
+    """One call sequence of a step object captured in a HIP graph and replayed.
+
+    The graph holds the step's own kernel launches on its own buffers (no allocation, no memset,
+    no synchronisation happens inside the entry points), so a replay is the same work as
+    ``step.run()`` with one host launch instead of one per kernel.  Inputs are read at every
+    replay: write new values into the step's input tensors in place between replays.  The
+    step's tensors must stay alive as long as the graph.
+    """
+
+    def __init__(self, step, warmup: int = 2):
+        self.step = step
+        side = torch.cuda.Stream()  # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                step.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            step.run()
+        torch.cuda.synchronize()
+
+    def run(self):
+        self.graph.replay()
