@@ -28,7 +28,8 @@
 // values stream into LDS in 32-token tiles through direct global-to-LDS transfers, three tiles in
 // flight.  Scores are computed transposed, S^T = [K | k^R] . Q^T (tokens on M, queries on N, 12 k-steps), so every
 // lane holds 16 scores of one query and the softmax stays in the lane plus one v_permlane32_swap.
-// Online softmax with a running maximum; the accumulator is rescaled only when a maximum moved.
+// Online softmax with a running maximum; the accumulator is rescaled by a factor that is 1 where
+// the query's maximum stayed (branch-free).
 // The weighted sum is accumulated transposed, O^T += V^T . P^T, with V^T from transposing reads in
 // the token order of the score layout.  Output o [b][q][h][128] float32 and lse [b][q][h].
 
