@@ -3,7 +3,8 @@ item: E4M3 on the 512-wide latent with a per-token scale).
 
 * mla_quantize_rows_fp8 (bf16 rows -> 656-byte FP8 rows) must equal the oracle's quantisation
   byte for byte: the codes are integers decided from the same bf16 values in exact arithmetic.
-* The decode, the balanced decode and the prefill over an FP8 pool must match the oracle run on
+* The decode, the balanced decode, the prefill and the multi-token verify over an FP8 pool must
+  match the oracle run on
   the latents that pool holds (code value x scale, dequantised by the oracle from its own
   quantisation), with the bf16 tolerances of the absorbed path.  Because code value x 2^e is
   exact in bf16, the FP8 decode must also be bitwise identical to the bf16 decode over a pool
@@ -179,6 +180,34 @@ def test_fp8_prefill_small():
             ref = view.prefill_row(b, i, HEADS)
             assert_abs_close(_np(st.lse)[b, i, HEADS], ref["lse"][HEADS], tol, f"lse ({b},{i})")
             assert_rms_close(_np(st.out)[b, i, HEADS], ref["o"][HEADS], tol, f"o ({b},{i})")
+
+
+def test_fp8_verify_small():
+    """Multi-token verify over an FP8 pool (draft rows through the balanced decode): every row on
+    three heads against the oracle's prefill rows on the dequantised latents, and bitwise equal to
+    the verify over the bf16 pool that holds those values."""
+    w = gen.Workload(name="fp8_verify", seed=75, kind="prefill", batch=4, ctx_range=(1, 300), q_len=4,
+                     random_pages=True)
+    inp = gen.make_prefill_inputs(w)
+    pool8 = oracle_fp8_pool(inp["pool"])
+    inp8 = dict(inp, pool=pool8)
+    note(f"fp8 verify small lens={inp['lens'].tolist()}")
+    st = runner.VerifyStep(inp8, DEV, n_units=16, flags=F8)
+    st.run()
+    torch.cuda.synchronize()
+    view = Fp8View(inp8, pool8)
+    tol = TOL["bf16"]
+    for b in range(w.batch):
+        for i in range(w.q_len):
+            ref = view.prefill_row(b, i, HEADS)
+            assert_abs_close(_np(st.lse)[b, i, HEADS], ref["lse"][HEADS], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i, HEADS], ref["o"][HEADS], tol, f"o ({b},{i})")
+    sd = runner.VerifyStep(dict(inp, pool=dequantized_bf16_pool(pool8)), DEV, n_units=16)
+    sd.run()
+    torch.cuda.synchronize()
+    for name in ("out", "lse", "z"):
+        a, b = getattr(st, name).cpu().numpy(), getattr(sd, name).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"FP8 verify {name} differs from the bf16 verify"
 
 
 @pytest.mark.parametrize("name,rows,d_model", [("v3_kv_append_b64", None, None), ("kv_edge", 37, 768)])
