@@ -4,9 +4,8 @@ item: E4M3 on the 512-wide latent with a per-token scale).
 * mla_quantize_rows_fp8 (bf16 rows -> 656-byte FP8 rows) must equal the oracle's quantisation
   byte for byte: the codes are integers decided from the same bf16 values in exact arithmetic.
 * The decode, the balanced decode, the prefill and the multi-token verify over an FP8 pool must
-  match the oracle run on
-  the latents that pool holds (code value x scale, dequantised by the oracle from its own
-  quantisation), with the bf16 tolerances of the absorbed path.  Because code value x 2^e is
+  match the oracle run on the latents that pool holds (code value x scale, dequantised by the
+  oracle from its own quantisation), with the bf16 tolerances of the absorbed path.  Because code value x 2^e is
   exact in bf16, the FP8 decode must also be bitwise identical to the bf16 decode over a pool
   that holds those values.
 * mla_kv_append with the flag writes FP8 rows: its latents come from fp32 sums, the oracle's from
