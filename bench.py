@@ -141,8 +141,9 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
                       f"unabsorbed fp64 NumPy) in {el:.1f} s"}
 
 
-def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
-    """The fp64 oracle on prefill rows of the same workload until `seconds` pass (algorithmic flops/s)."""
+def cpu_baseline_prefill(inp: dict, seconds: float, unabsorbed: bool = False) -> dict:
+    """The fp64 oracle on prefill rows of the same workload until `seconds` pass (algorithmic flops/s:
+    2,176 per visible (query head, key) pair for the absorbed path, 640 for the unabsorbed one)."""
     import oracle.mla_oracle as O
     from mla_workloads import gen
 
@@ -158,7 +159,8 @@ def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
         p = int(inp["q_start"][b]) + i
         O.attention(gen.as_f64(inp["q_c"][b, i], dt), gen.as_f64(inp["q_r"][b, i], dt), p, cache[:p + 1], w_uk, w_uv,
                     w.d_c, base=w.rope_base)
-        flops += (p + 1) * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+        per_pair = 2 * (w.d_k + w.d_r) + 2 * w.d_v if unabsorbed else 2 * (w.d_c + w.d_r) + 2 * w.d_c
+        flops += (p + 1) * w.n_heads * per_pair
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -166,7 +168,112 @@ def cpu_baseline_prefill(inp: dict, seconds: float) -> dict:
     return {"value": round(flops / el / 1e12, 9), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
             "cpu_model": _cpu_model(),
             "sample": f"first {n} of {w.q_len} query rows of sequence 0 (all {w.n_heads} heads, unabsorbed fp64 "
-                      f"NumPy; algorithmic absorbed flops counted) in {el:.1f} s"}
+                      f"NumPy; algorithmic {'unabsorbed attention' if unabsorbed else 'absorbed'} flops counted) "
+                      f"in {el:.1f} s"}
+
+
+def cpu_baseline_fp8(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle on the FP8 cache of the same batch, whole sequences until `seconds` pass:
+    its own E4M3 quantisation of each sequence's latents, their dequantisation, then attention
+    (GB/s of 656-byte FP8 rows)."""
+    import numpy as np
+
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = inp["dtype"]
+    w_uk = gen.as_f64(inp["w_uk"], dt)
+    w_uv = gen.as_f64(inp["w_uv"], dt)
+    toks, n = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        L = int(inp["lens"][b])
+        rows = O.gather_rows(inp["pool"], inp["page_table"], b, L)
+        codes, scale = O.quantize_latents_fp8(gen.as_f64(rows[:, :w.d_c], dt))
+        cache = np.concatenate([O.dequantize_latents_fp8(codes, scale), gen.as_f64(rows[:, w.d_c:], dt)], axis=1)
+        O.attention(gen.as_f64(inp["q_c"][b], dt), gen.as_f64(inp["q_r"][b], dt), L - 1, cache, w_uk, w_uv,
+                    w.d_c, base=w.rope_base)
+        toks += L
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(toks * O.FP8_ROW_BYTES / el / 1e9, 6), "unit": "GB/s", "cores": _blas_threads(),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"first {n} of {w.batch} sequences ({toks} cached tokens as {O.FP8_ROW_BYTES}-byte FP8 rows, "
+                      f"quantised and dequantised by the oracle, all {w.n_heads} heads, unabsorbed fp64 NumPy) "
+                      f"in {el:.1f} s"}
+
+
+def cpu_baseline_verify(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle on the draft rows of the same verify batch until `seconds` pass: row (b, i)
+    attends over keys t <= q_start[b] + i, t < len[b] (draft tokens per second)."""
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = inp["dtype"]
+    w_uk = gen.as_f64(inp["w_uk"], dt)
+    w_uv = gen.as_f64(inp["w_uv"], dt)
+    n = 0
+    t0 = time.perf_counter()
+    done = False
+    for b in range(w.batch):
+        L = int(inp["lens"][b])
+        cache = gen.as_f64(O.gather_rows(inp["pool"], inp["page_table"], b, L), dt)
+        for i in range(w.q_len):
+            p = int(inp["q_start"][b]) + i
+            keys = min(p + 1, L)
+            if keys > 0:
+                O.attention(gen.as_f64(inp["q_c"][b, i], dt), gen.as_f64(inp["q_r"][b, i], dt), p, cache[:keys],
+                            w_uk, w_uv, w.d_c, base=w.rope_base)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                done = True
+                break
+        if done:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(n / el, 4), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"first {n} of {w.batch * w.q_len} draft rows (all {w.n_heads} heads, unabsorbed fp64 NumPy) "
+                      f"in {el:.1f} s"}
+
+
+def cpu_baseline_precomposed(inp: dict, seconds: float) -> dict:
+    """The fp64 oracle's two per-step precomposed products on a sample of the same rows, scaled to
+    all rows (ms per step).  The precomposition itself, an offline step, is done first and not
+    timed."""
+    import oracle.mla_oracle as O
+    from mla_workloads import gen
+
+    w = inp["workload"]
+    dt = w.dtype
+    R = int(inp["c_q"].shape[0])
+    wa = O.precompose_query_weights(gen.as_f64(inp["w_uq"], dt), gen.as_f64(inp["w_uk"], dt))
+    w_uvo = O.precompose_out_weights(gen.as_f64(inp["w_uv"], dt), gen.as_f64(inp["w_o"], dt))
+    w_qr = gen.as_f64(inp["w_qr"], dt)
+    nq = 0
+    t0 = time.perf_counter()
+    while nq < R:
+        O.absorbed_query_precomposed(gen.as_f64(inp["c_q"][nq], dt), wa, w_qr, int(inp["pos"][nq]), base=w.rope_base)
+        nq += 1
+        if time.perf_counter() - t0 >= seconds / 2:
+            break
+    tq = (time.perf_counter() - t0) / nq
+    no = 0
+    t0 = time.perf_counter()
+    while no < R:
+        O.out_proj_fused(inp["z"][no:no + 1].astype("float64"), w_uvo)
+        no += 1
+        if time.perf_counter() - t0 >= seconds / 2:
+            break
+    to = (time.perf_counter() - t0) / no
+    return {"value": round((tq + to) * R * 1e3, 3), "unit": "ms", "cores": _blas_threads(), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"fused query on {nq} and fused output on {no} of {R} rows (fp64 NumPy, precomposition "
+                      f"untimed), scaled to {R} rows"}
 
 
 def bench_prefill_unabsorbed(args, w) -> dict:
@@ -221,7 +328,7 @@ def bench_prefill_unabsorbed(args, w) -> dict:
                      "traffic": None, "ms_per_launch": round(ms_attn, 6), "algorithmic_flops_per_launch": flops_attn},
         "decompress": {"ms_per_launch": round(ms_step - ms_attn, 6), "algorithmic_flops_per_launch": flops_dec,
                        "tflops": round(flops_dec / ((ms_step - ms_attn) * 1e-3) / 1e12, 3)},
-    }
+    } | ({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_prefill(inp, args.cpu_seconds, True)})
 
 
 def bench_prefill(args, w) -> dict:
@@ -350,7 +457,7 @@ def bench_verify(args, w) -> dict:
         "roofline_mfma": {"achieved": round(flops / (ms_dec * 1e-3) / 1e12, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(flops / (ms_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "prefill_chunk_ms_per_step": round(ms_pf, 6),
-    }
+    } | ({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_verify(inp, args.cpu_seconds)})
 
 
 def bench_precomposed(args, w) -> dict:
@@ -427,7 +534,7 @@ def bench_precomposed(args, w) -> dict:
         "roofline": {"bound": "hbm", "kernel": "mla_out_proj_fused", "achieved": round(ach, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                      "ms_per_launch": round(ms["fused_output"], 6), "algorithmic_bytes_per_launch": bytes_fused_out},
-    }
+    } | ({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_precomposed(inp, args.cpu_seconds)})
 
 
 def cpu_baseline_kv_append(inp: dict, seconds: float) -> dict:
@@ -716,7 +823,7 @@ def main() -> int:
                           "frac": round(flops_decode / (ms_decode * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = (cpu_baseline_fp8 if args.fp8 else cpu_baseline)(inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
 

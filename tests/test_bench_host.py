@@ -57,3 +57,28 @@ def test_cpu_baseline_record():
     assert rec["sample"].startswith("first 1 of 3 sequences")
     assert f"({int(inp['lens'][0])} cached tokens" in rec["sample"]
     assert np.isfinite(rec["value"])
+
+
+def _prefill_tiny():
+    w = gen.Workload(name="cpu_tiny_prefill", seed=6, kind="prefill", batch=2, ctx_range=(5, 40), q_len=3,
+                     random_pages=True)
+    return gen.make_prefill_inputs(w)
+
+
+def test_cpu_baselines_of_the_other_benches():
+    """The oracle legs of the FP8, verify, unabsorbed-prefill and precomposed benches, on tiny
+    workloads: each returns the record fields in its bench's own unit."""
+    w = gen.Workload(name="cpu_tiny", seed=5, kind="decode", batch=3, ctx_range=(20, 90), random_pages=True)
+    rec = bench.cpu_baseline_fp8(gen.make_decode_inputs(w), seconds=0.0)
+    assert rec["unit"] == "GB/s" and rec["value"] > 0 and "656-byte FP8 rows" in rec["sample"]
+    inp = _prefill_tiny()
+    rec = bench.cpu_baseline_verify(inp, seconds=0.0)
+    assert rec["unit"] == "tokens/s" and rec["value"] > 0 and rec["sample"].startswith("first 1 of 6 draft rows")
+    rec = bench.cpu_baseline_prefill(inp, seconds=0.0, unabsorbed=True)
+    assert rec["unit"] == "TFLOP/s" and rec["value"] > 0 and "unabsorbed attention" in rec["sample"]
+    wp = gen.Workload(name="cpu_tiny_pc", seed=7, kind="precomposed", batch=4, n_heads=2, d_c=16, d_r=4, d_k=8,
+                      d_v=8, d_cq=12, d_model=20)
+    rec = bench.cpu_baseline_precomposed(gen.make_precomposed_inputs(wp), seconds=0.0)
+    assert rec["unit"] == "ms" and rec["value"] > 0 and rec["kind"] == "oracle"
+    for r in (rec,):
+        assert isinstance(r["cores"], int) and r["cpu_model"]
