@@ -10,6 +10,8 @@
  *   - Device pointers are plain device addresses owned by the caller.  The library allocates
  *     nothing, keeps no state between calls and retains no pointer after a call returns.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the null stream).
+ *     No call allocates, synchronises or enqueues a memset or copy: only kernel launches go
+ *     on the stream, so any sequence of calls can be captured in a HIP graph and replayed.
  *   - Host-visible arguments are validated before anything is launched; a failed check returns
  *     an MLA_ERR_* code and touches no device memory.  A failed launch returns MLA_ERR_HIP.
  *     Faults during execution surface at the caller's next synchronisation.
