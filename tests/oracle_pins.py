@@ -465,10 +465,35 @@ def pin_precomposed_weights():
     _close(fused[:, 1:5], np.zeros((4, 4)), 0.0, "selector zeros")
 
 
+def pin_rms_normalize():
+    """RMSNorm with unit gain ([ase] Fig. 1 note: a norm follows the latent; eps and gain are not on
+    the pages, the reading is eps = 1e-6 and gain 1) against the library routine (torch's rms_norm on
+    the CPU in float64) and closed forms: a constant row a gives a / sqrt(a^2 + eps) everywhere; with
+    eps = 0 every row has mean square exactly 1 and the result does not change when a row is scaled
+    by a positive factor; the norm acts on each row alone."""
+    r = _rng(41)
+    x = r.standard_normal((6, 512)) * r.uniform(0.01, 30.0, size=(6, 1))
+    for eps in (1e-6, 0.3):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), weight=None, eps=eps).numpy()
+        _close(O.rms_normalize(x, eps), ref, 1e-12, f"library rms_norm eps={eps}")
+    for a in (2.0, -0.5, 1e-3):
+        for eps in (1e-6, 0.25):
+            _close(O.rms_normalize(np.full((1, 7), a), eps), np.full((1, 7), a / math.sqrt(a * a + eps)), 1e-15,
+                   f"constant row {a} eps={eps}")
+    y = O.rms_normalize(x, 0.0)
+    _close(np.mean(y * y, axis=-1), np.ones(6), 1e-12, "unit mean square at eps 0")
+    _close(O.rms_normalize(x * np.array([[3.0], [0.01], [7.5], [1.0], [250.0], [0.5]]), 0.0), y, 1e-12,
+           "positive row scaling")
+    _close(O.rms_normalize(x[2:3], 1e-6), O.rms_normalize(x, 1e-6)[2:3], 0.0, "rows are independent")
+    # eps decides rows of tiny magnitude: x = +-1e-3 has mean square 1e-6, so the result is x / sqrt(2e-6)
+    t = np.array([[1e-3, -1e-3, 1e-3, -1e-3]])
+    _close(O.rms_normalize(t, 1e-6), t / math.sqrt(2e-6), 1e-12, "eps on a tiny row")
+
+
 ALL_PINS = {f.__name__: f for f in (
     pin_score_example, pin_key_absorption, pin_value_absorption, pin_cache_accounting,
     pin_rope_closed_forms, pin_rope_complex_form, pin_rope_relative,
     pin_sdpa_textbook, pin_sdpa_general, pin_prefill_causal, pin_loops_twin,
     pin_absorbed_equals_decompressed, pin_softmax_and_special_cases, pin_merge_partials,
-    pin_gather_rows, pin_projections, pin_fp8_e4m3, pin_fp8_scale_and_rows, pin_precomposed_weights,
+    pin_gather_rows, pin_projections, pin_fp8_e4m3, pin_fp8_scale_and_rows, pin_precomposed_weights, pin_rms_normalize,
 )}

@@ -103,6 +103,26 @@ def _scale_exponent_floor(amax):
     return np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0).astype(np.int64)
 
 
+def _rms_sum_not_mean(c, eps=1e-6):
+    c = np.asarray(c, F64)
+    return c / np.sqrt(np.sum(c * c, axis=-1, keepdims=True) + eps)
+
+
+def _rms_eps_outside_sqrt(c, eps=1e-6):
+    c = np.asarray(c, F64)
+    return c / (np.sqrt(np.mean(c * c, axis=-1, keepdims=True)) + eps)
+
+
+def _rms_multiplies(c, eps=1e-6):
+    c = np.asarray(c, F64)
+    return c * np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+
+
+def _rms_wrong_axis(c, eps=1e-6):
+    c = np.asarray(c, F64)
+    return c / np.sqrt(np.mean(c * c, axis=0, keepdims=True) + eps)
+
+
 MUTANTS = {
     "precompose_query_untransposed_key": ("precompose_query_weights", lambda uq, uk: np.einsum(
         "hqk,hkc->hqc", np.asarray(uq, F64), np.asarray(uk, F64).reshape(uk.shape[0], uk.shape[2], uk.shape[1]))),
@@ -128,6 +148,10 @@ MUTANTS = {
     "lse_missing_max": ("softmax_lse", _softmax_lse_no_max),
     "merge_without_normalising": ("merge_partials", _merge_unnormalised),
     "gather_ignores_page_table": ("gather_rows", _gather_wrong),
+    "rms_sum_instead_of_mean": ("rms_normalize", _rms_sum_not_mean),
+    "rms_eps_outside_sqrt": ("rms_normalize", _rms_eps_outside_sqrt),
+    "rms_multiplies_instead_of_divides": ("rms_normalize", _rms_multiplies),
+    "rms_over_wrong_axis": ("rms_normalize", _rms_wrong_axis),
     "query_projections_swapped": ("query_parts", lambda h, dq, uq, qr: (
         np.asarray(h, F64) @ dq, np.einsum("...c,hck->...hk", np.asarray(h, F64) @ dq, np.asarray(qr, F64)),
         np.einsum("...c,hcr->...hr", np.asarray(h, F64) @ dq, np.asarray(uq, F64)))),
