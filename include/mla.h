@@ -41,7 +41,8 @@ typedef enum {
   MLA_ERR_DTYPE = 3,       /* unknown dtype code */
   MLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
   MLA_ERR_UNSUPPORTED = 5, /* well-formed but beyond what the kernels implement */
-  MLA_ERR_HIP = 6          /* a HIP runtime call or a kernel launch failed */
+  MLA_ERR_HIP = 6,         /* a HIP runtime call or a kernel launch failed */
+  MLA_ERR_WORKSPACE = 7    /* a caller-provided workspace is smaller than the call needs */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
@@ -113,33 +114,54 @@ int32_t mla_decode_num_splits(int32_t max_len, int32_t split_tokens);
 int32_t mla_decode_uses_mfma(const mla_dims* dims, const mla_cache* cache, int32_t split_tokens);
 int32_t mla_prefill_uses_mfma(const mla_dims* dims, const mla_cache* cache);
 
+/* Split-K workspace.  The split-K decode calls write one partial result per (segment, head) into a
+ * caller-provided workspace that the combine calls then read.  A workspace of `slots` partial
+ * slots holds
+ *   o_part   float [slots, H, d_c]   at byte 0
+ *   lse_part float [slots, H]        at byte mla_partials_lse_offset(dims, slots)
+ *                                    (the o_part bytes rounded up to a multiple of 256)
+ * and spans mla_partials_bytes(dims, slots) bytes.  Both return 0 for invalid arguments.
+ * The split into pieces and the merge are not on the pages; they are an exact rewrite of the
+ * one-pass softmax of [ase] Fig. 2 (see mla_combine).  A serving system sizes the workspace once
+ * ([molayo] key concept 5: a page table of latents served by custom attention kernels). */
+size_t mla_partials_lse_offset(const mla_dims* dims, int32_t slots);
+size_t mla_partials_bytes(const mla_dims* dims, int32_t slots);
+
+/* Workspace bytes mla_decode_partial needs for these arguments: mla_partials_bytes for
+ * batch * mla_decode_num_splits(max_len, split_tokens) slots (0 for invalid arguments). */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, const mla_cache* cache, int32_t max_len,
+                                  int32_t split_tokens);
+
 /* Split-K decode over the latent cache, one query token per sequence (the newest, at position
  * seq_lens[b]-1).  Chunk i of sequence b covers tokens [i*split_tokens, (i+1)*split_tokens)
  * intersected with [0, seq_lens[b]).  For each chunk and head it writes the chunk-local softmax
- * result ([ase] Fig. 2 scores over the 576-wide concatenation; Fig. 4: the weighted latent
- * z = a.C, the rotary part is never summed):
- *   o_part[b,i,h,:] = sum_t softmax_t(s) c_t  (normalised within the chunk)
- *   lse_part[b,i,h] = ln sum_t exp(s_t)        with s_t = q_hat . row_t / log2(e)
+ * result into slot b*S + i of the workspace ([ase] Fig. 2 scores over the 576-wide concatenation;
+ * Fig. 4: the weighted latent z = a.C, the rotary part is never summed):
+ *   o_part[b*S+i,h,:] = sum_t softmax_t(s) c_t  (normalised within the chunk)
+ *   lse_part[b*S+i,h] = ln sum_t exp(s_t)        with s_t = q_hat . row_t / log2(e)
  * An empty chunk writes lse_part = -inf and may leave its o_part row untouched: the combine gives
  * it zero weight and never reads it.
- *   q_hat    device dtype [batch, H, d_c + d_r]   (as written by mla_absorb_query)
+ *   q_hat    device [batch, H, d_c + d_r]   (as written by mla_absorb_query)
  *   max_len  host bound >= every seq_lens[b]; sets S = mla_decode_num_splits(max_len, split_tokens)
  *   split_tokens  > 0 and a multiple of cache->page_size
- *   o_part   device float [batch, S, H, d_c]
- *   lse_part device float [batch, S, H]                                                          */
+ *   workspace      device, workspace_bytes long, 16-byte aligned
+ *   workspace_bytes  MLA_ERR_WORKSPACE (before any launch) when below
+ *                  mla_decode_workspace_bytes(dims, cache, max_len, split_tokens)              */
 mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
-                              int32_t max_len, int32_t split_tokens, float* o_part, float* lse_part,
+                              int32_t max_len, int32_t split_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
 
 /* Log-sum-exp merge of split-K partials: LSE = ln sum_i exp(lse_i),
  * z = sum_i exp(lse_i - LSE) o_i.  Over any split this equals the single-pass softmax of
  * [ase] Fig. 2.  All chunks empty gives z = 0 and lse = -inf.
- *   o_part   device float [batch, n_splits, H, d_c]
- *   lse_part device float [batch, n_splits, H]
- *   z        device float [batch, H, d_c]       (output)
+ *   workspace  device, partials of batch * n_splits slots in the layout above, slot b*n_splits + i
+ *              holding chunk i of sequence b (as mla_decode_partial writes them)
+ *   workspace_bytes  MLA_ERR_WORKSPACE when below mla_partials_bytes(dims, batch * n_splits)
+ *   z        device float [batch, H, d_c]       (output; float32 for either dtype: the weighted
+ *                                                 latent keeps its precision into mla_out_proj)
  *   lse      device float [batch, H] or NULL   (output)                                          */
-mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const float* o_part,
-                       const float* lse_part, float* z, float* lse, void* stream);
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const void* workspace,
+                       size_t workspace_bytes, float* z, float* lse, void* stream);
 
 /* Work-balanced split-K ([ase] Fig. 2 softmax over all cached positions, evaluated piecewise and
  * merged as in mla_combine).  Fixed-size chunks leave most of the GPU idle on ragged batches; this
@@ -161,23 +183,28 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, co
 /* Number of partial slots of the balanced split: n_units + batch - 1 (-1 on bad arguments). */
 int32_t mla_balanced_num_slots(int32_t batch, int32_t n_units);
 
+/* Workspace bytes mla_decode_partial_balanced needs: mla_partials_bytes for
+ * mla_balanced_num_slots(batch, n_units) slots (0 for invalid arguments). */
+size_t mla_decode_balanced_workspace_bytes(const mla_dims* dims, const mla_cache* cache, int32_t n_units);
+
 /* Balanced split-K decode: writes, for every non-empty segment (w, b) and head h, the same
- * chunk-local pair as mla_decode_partial over the segment's tokens:
+ * chunk-local pair as mla_decode_partial over the segment's tokens into slot w + b:
  *   o_part[w+b,h,:]  (normalised),  lse_part[w+b,h]  (natural log)
  *   n_units  1 .. MLA_BALANCED_MAX_UNITS
- *   o_part   device float [mla_balanced_num_slots(batch, n_units), H, d_c]
- *   lse_part device float [mla_balanced_num_slots(batch, n_units), H]
+ *   workspace, workspace_bytes  as for mla_decode_partial; MLA_ERR_WORKSPACE when below
+ *            mla_decode_balanced_workspace_bytes(dims, cache, n_units)
  * MLA_ERR_UNSUPPORTED when batch * (max_pages*page_size / MLA_BALANCED_TILE + 9) >= 2^31 - 2^12. */
 mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
-                                       int32_t n_units, float* o_part, float* lse_part, void* stream);
+                                       int32_t n_units, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Merge of the balanced partials: for every sequence, the log-sum-exp merge of mla_combine over
  * the slots of its non-empty segments (none: z = 0, lse = -inf).  cache supplies seq_lens, batch,
  * page_size and max_pages (pool and page_table are not read but must be valid pointers).
+ *   workspace, workspace_bytes  as written by mla_decode_partial_balanced with the same n_units
  *   z   device float [batch, H, d_c]   (output)
  *   lse device float [batch, H] or NULL (output)                                                  */
 mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
-                                const float* o_part, const float* lse_part, float* z, float* lse, void* stream);
+                                const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream);
 
 /* Value up-projection applied once after the weighted sum ([ase] "Value 투영을 가중합 뒤로
  * 옮기기", Fig. 4 equation; [huny] section 2, value absorption):
@@ -260,7 +287,8 @@ mla_status mla_precompose_out(const mla_dims* dims, int32_t d_model, const void*
  * RoPE_pos[r](c_q[r] . W_QR[h])] * sm_scale * log2(e), rounded to bf16 once (the layout and
  * scaling of mla_absorb_query).  c_q bf16 [rows, d_cq]; w_qcat from mla_precompose_query; pos
  * device int32 [rows]; q_hat bf16 [rows, H, d_c + d_r].  workspace: device float32 scratch of at
- * least mla_absorb_query_precomposed_workspace_bytes bytes (caller-owned, overwritten). */
+ * least mla_absorb_query_precomposed_workspace_bytes bytes (caller-owned, overwritten; smaller:
+ * MLA_ERR_WORKSPACE). */
 size_t mla_absorb_query_precomposed_workspace_bytes(const mla_dims* dims, int32_t d_cq, int32_t rows);
 mla_status mla_absorb_query_precomposed(const mla_dims* dims, int32_t d_cq, const void* c_q, const void* w_qcat,
                                         const int32_t* pos, int32_t rows, void* q_hat, float* workspace,
@@ -313,7 +341,7 @@ mla_status mla_project_query(const mla_dims* dims, int32_t d_model, int32_t d_cq
  *   seq_ids, positions device int32 [rows]; two rows must not name the same token.
  *   workspace: device fp32 scratch of at least mla_kv_append_workspace_bytes(dims, d_model, rows)
  *   bytes, owned by the caller, contents ignored and overwritten (NULL allowed when that size
- *   is 0).  A smaller workspace_bytes gives MLA_ERR_SHAPE.
+ *   is 0).  A smaller workspace_bytes gives MLA_ERR_WORKSPACE.
  * bf16 with d_c 512, d_r 64 and d_model a multiple of 256 runs on MFMA (a split-K product into
  * the workspace, then one wave per row for the norm, the rotation and the store); every other
  * shape runs the generic kernel, which needs no workspace. */

@@ -21,6 +21,7 @@ MLA_ERR_DTYPE = 3
 MLA_ERR_ALIGN = 4
 MLA_ERR_UNSUPPORTED = 5
 MLA_ERR_HIP = 6
+MLA_ERR_WORKSPACE = 7
 
 MLA_F32 = 0
 MLA_BF16 = 1
@@ -63,11 +64,15 @@ _SIGNATURES = {
     "mla_decode_num_splits": (_I32, [_I32, _I32]),
     "mla_decode_uses_mfma": (_I32, [_PD, _PC, _I32]),
     "mla_prefill_uses_mfma": (_I32, [_PD, _PC]),
-    "mla_decode_partial": (_I32, [_PD, _PC, _VP, _I32, _I32, _VP, _VP, _VP]),
-    "mla_combine": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "mla_partials_lse_offset": (ctypes.c_size_t, [_PD, _I32]),
+    "mla_partials_bytes": (ctypes.c_size_t, [_PD, _I32]),
+    "mla_decode_workspace_bytes": (ctypes.c_size_t, [_PD, _PC, _I32, _I32]),
+    "mla_decode_partial": (_I32, [_PD, _PC, _VP, _I32, _I32, _VP, ctypes.c_size_t, _VP]),
+    "mla_combine": (_I32, [_PD, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_balanced_num_slots": (_I32, [_I32, _I32]),
-    "mla_decode_partial_balanced": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP]),
-    "mla_combine_balanced": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "mla_decode_balanced_workspace_bytes": (ctypes.c_size_t, [_PD, _PC, _I32]),
+    "mla_decode_partial_balanced": (_I32, [_PD, _PC, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
+    "mla_combine_balanced": (_I32, [_PD, _PC, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
@@ -173,14 +178,27 @@ def mla_absorb_query(d: MlaDims, q_c, q_r, w_uk, pos, rows: int, q_hat, stream=N
                                       _addr(q_hat), _stream(stream)), "mla_absorb_query")
 
 
-def mla_decode_partial(d: MlaDims, c: MlaCache, q_hat, max_len: int, split_tokens: int, o_part, lse_part,
-                       stream=None) -> None:
+def mla_partials_lse_offset(d: MlaDims, slots: int) -> int:
+    return int(library().mla_partials_lse_offset(ctypes.byref(d), slots))
+
+
+def mla_partials_bytes(d: MlaDims, slots: int) -> int:
+    return int(library().mla_partials_bytes(ctypes.byref(d), slots))
+
+
+def mla_decode_workspace_bytes(d: MlaDims, c: MlaCache, max_len: int, split_tokens: int) -> int:
+    return int(library().mla_decode_workspace_bytes(ctypes.byref(d), ctypes.byref(c), max_len, split_tokens))
+
+
+def mla_decode_partial(d: MlaDims, c: MlaCache, q_hat, max_len: int, split_tokens: int, workspace,
+                       workspace_bytes: int, stream=None) -> None:
     _check(library().mla_decode_partial(ctypes.byref(d), ctypes.byref(c), _addr(q_hat), max_len, split_tokens,
-                                        _addr(o_part), _addr(lse_part), _stream(stream)), "mla_decode_partial")
+                                        _addr(workspace), workspace_bytes, _stream(stream)), "mla_decode_partial")
 
 
-def mla_combine(d: MlaDims, batch: int, n_splits: int, o_part, lse_part, z, lse=None, stream=None) -> None:
-    _check(library().mla_combine(ctypes.byref(d), batch, n_splits, _addr(o_part), _addr(lse_part), _addr(z),
+def mla_combine(d: MlaDims, batch: int, n_splits: int, workspace, workspace_bytes: int, z, lse=None,
+                stream=None) -> None:
+    _check(library().mla_combine(ctypes.byref(d), batch, n_splits, _addr(workspace), workspace_bytes, _addr(z),
                                  _addr(lse), _stream(stream)), "mla_combine")
 
 
@@ -188,17 +206,21 @@ def mla_balanced_num_slots(batch: int, n_units: int) -> int:
     return library().mla_balanced_num_slots(batch, n_units)
 
 
-def mla_decode_partial_balanced(d: MlaDims, c: MlaCache, q_hat, n_units: int, o_part, lse_part,
+def mla_decode_balanced_workspace_bytes(d: MlaDims, c: MlaCache, n_units: int) -> int:
+    return int(library().mla_decode_balanced_workspace_bytes(ctypes.byref(d), ctypes.byref(c), n_units))
+
+
+def mla_decode_partial_balanced(d: MlaDims, c: MlaCache, q_hat, n_units: int, workspace, workspace_bytes: int,
                                 stream=None) -> None:
     _check(library().mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), _addr(q_hat), n_units,
-                                                 _addr(o_part), _addr(lse_part), _stream(stream)),
+                                                 _addr(workspace), workspace_bytes, _stream(stream)),
            "mla_decode_partial_balanced")
 
 
-def mla_combine_balanced(d: MlaDims, c: MlaCache, n_units: int, o_part, lse_part, z, lse=None,
+def mla_combine_balanced(d: MlaDims, c: MlaCache, n_units: int, workspace, workspace_bytes: int, z, lse=None,
                          stream=None) -> None:
-    _check(library().mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n_units, _addr(o_part),
-                                          _addr(lse_part), _addr(z), _addr(lse), _stream(stream)),
+    _check(library().mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n_units, _addr(workspace),
+                                          workspace_bytes, _addr(z), _addr(lse), _stream(stream)),
            "mla_combine_balanced")
 
 

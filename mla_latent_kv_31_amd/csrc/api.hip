@@ -67,6 +67,31 @@ mla_status ptr_ok(const void* p) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Split-K workspace layout: o_part float [slots, H, d_c] at byte 0, lse_part float [slots, H] at the
+// o_part size rounded up to 256 bytes.
+size_t partials_lse_offset(const Dims& d, int64_t slots) {
+  const size_t o = size_t(slots) * size_t(d.H) * size_t(d.dc) * sizeof(float);
+  return (o + 255) & ~size_t(255);
+}
+size_t partials_bytes(const Dims& d, int64_t slots) {
+  return partials_lse_offset(d, slots) + size_t(slots) * size_t(d.H) * sizeof(float);
+}
+
+// The partials of a checked workspace.
+struct Partials {
+  float* o;
+  float* lse;
+};
+mla_status check_workspace(const Dims& d, int64_t slots, const void* ws, size_t ws_bytes, Partials* out) {
+  if (!ws) return MLA_ERR_NULL;
+  if (!aligned16(ws)) return MLA_ERR_ALIGN;
+  if (ws_bytes < partials_bytes(d, slots)) return MLA_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(const_cast<void*>(ws));
+  out->o = reinterpret_cast<float*>(base);
+  out->lse = reinterpret_cast<float*>(base + partials_lse_offset(d, slots));
+  return MLA_OK;
+}
+
 bool cache_fp8(const mla_dims* dims) { return (dims->flags & MLA_FLAG_CACHE_FP8) != 0; }
 bool generic_forced(const mla_dims* dims) { return (dims->flags & MLA_FLAG_FORCE_GENERIC) != 0; }
 
@@ -92,6 +117,7 @@ const char* mla_status_str(mla_status s) {
     case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: a device pointer is not 16-byte aligned";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: well-formed but beyond the implemented limits";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: the workspace is smaller than the call needs";
   }
   return "unknown mla_status";
 }
@@ -134,41 +160,62 @@ mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q
   return hip_status(launch_absorb_generic(d, q_c, q_r, w_uk, pos, rows, q_hat, (hipStream_t)stream));
 }
 
-mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t max_len,
-                              int32_t split_tokens, float* o_part, float* lse_part, void* stream) {
+size_t mla_partials_lse_offset(const mla_dims* dims, int32_t slots) {
+  Dims d;
+  if (check_dims(dims, &d) != MLA_OK || slots < 0) return 0;
+  return partials_lse_offset(d, slots);
+}
+
+size_t mla_partials_bytes(const mla_dims* dims, int32_t slots) {
+  Dims d;
+  if (check_dims(dims, &d) != MLA_OK || slots < 0) return 0;
+  return partials_bytes(d, slots);
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, const mla_cache* cache, int32_t max_len,
+                                  int32_t split_tokens) {
   Dims d;
   Cache c;
+  if (check_dims(dims, &d) != MLA_OK || check_cache(cache, &c) != MLA_OK) return 0;
+  if (split_tokens < 1 || max_len < 0) return 0;
+  return partials_bytes(d, int64_t(c.batch) * mla_decode_num_splits(max_len, split_tokens));
+}
+
+mla_status mla_decode_partial(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t max_len,
+                              int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  Cache c;
+  Partials p;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   MLA_TRY(ptr_ok(q_hat));
-  MLA_TRY(ptr_ok(o_part));
-  MLA_TRY(ptr_ok(lse_part));
   if (split_tokens < 1 || split_tokens % c.page_size != 0) return MLA_ERR_SHAPE;
   if (max_len < 0 || int64_t(max_len) > int64_t(c.max_pages) * c.page_size) return MLA_ERR_SHAPE;
   const int S = mla_decode_num_splits(max_len, split_tokens);
+  MLA_TRY(check_workspace(d, int64_t(c.batch) * S, workspace, workspace_bytes, &p));
   const bool mfma = !generic_forced(dims) && decode_mfma_supported(d, c, split_tokens);
   if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0) return MLA_OK;
   if (mfma)
-    return hip_status(launch_decode_mfma(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream,
+    return hip_status(launch_decode_mfma(d, c, q_hat, S, split_tokens, p.o, p.lse, (hipStream_t)stream,
                                          cache_fp8(dims)));
-  return hip_status(launch_decode_generic(d, c, q_hat, S, split_tokens, o_part, lse_part, (hipStream_t)stream));
+  return hip_status(launch_decode_generic(d, c, q_hat, S, split_tokens, p.o, p.lse, (hipStream_t)stream));
 }
 
-mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const float* o_part,
-                       const float* lse_part, float* z, float* lse, void* stream) {
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t n_splits, const void* workspace,
+                       size_t workspace_bytes, float* z, float* lse, void* stream) {
   Dims d;
+  Partials p;
   MLA_TRY(check_dims(dims, &d));
   if (batch < 0 || n_splits < 1) return MLA_ERR_SHAPE;
   if (batch > 65535) return MLA_ERR_UNSUPPORTED;
-  MLA_TRY(ptr_ok(o_part));
-  MLA_TRY(ptr_ok(lse_part));
+  MLA_TRY(check_workspace(d, int64_t(batch) * n_splits, workspace, workspace_bytes, &p));
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
   if (batch == 0) return MLA_OK;
   if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_splits))
-    return hip_status(launch_combine_fast(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
-  return hip_status(launch_combine_generic(d, batch, n_splits, o_part, lse_part, z, lse, (hipStream_t)stream));
+    return hip_status(launch_combine_fast(d, batch, n_splits, p.o, p.lse, z, lse, (hipStream_t)stream));
+  return hip_status(launch_combine_generic(d, batch, n_splits, p.o, p.lse, z, lse, (hipStream_t)stream));
 }
 
 int32_t mla_balanced_num_slots(int32_t batch, int32_t n_units) {
@@ -176,40 +223,48 @@ int32_t mla_balanced_num_slots(int32_t batch, int32_t n_units) {
   return batch == 0 ? 0 : n_units + batch - 1;
 }
 
-mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
-                                       int32_t n_units, float* o_part, float* lse_part, void* stream) {
+size_t mla_decode_balanced_workspace_bytes(const mla_dims* dims, const mla_cache* cache, int32_t n_units) {
   Dims d;
   Cache c;
+  if (check_dims(dims, &d) != MLA_OK || check_cache(cache, &c) != MLA_OK) return 0;
+  const int32_t slots = mla_balanced_num_slots(c.batch, n_units);
+  return slots < 0 ? 0 : partials_bytes(d, slots);
+}
+
+mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                       int32_t n_units, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  Cache c;
+  Partials p;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   MLA_TRY(check_balanced(c, n_units));
   MLA_TRY(ptr_ok(q_hat));
-  MLA_TRY(ptr_ok(o_part));
-  MLA_TRY(ptr_ok(lse_part));
+  MLA_TRY(check_workspace(d, mla_balanced_num_slots(c.batch, n_units), workspace, workspace_bytes, &p));
   const bool mfma = !generic_forced(dims) && decode_mfma_supported(d, c, 0);
   if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0) return MLA_OK;
   if (mfma)
-    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream,
+    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, p.o, p.lse, (hipStream_t)stream,
                                                   cache_fp8(dims)));
-  return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, o_part, lse_part, (hipStream_t)stream));
+  return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, p.o, p.lse, (hipStream_t)stream));
 }
 
-mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units, const float* o_part,
-                                const float* lse_part, float* z, float* lse, void* stream) {
+mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream) {
   Dims d;
   Cache c;
+  Partials p;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   MLA_TRY(check_balanced(c, n_units));
-  MLA_TRY(ptr_ok(o_part));
-  MLA_TRY(ptr_ok(lse_part));
+  MLA_TRY(check_workspace(d, mla_balanced_num_slots(c.batch, n_units), workspace, workspace_bytes, &p));
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
   if (c.batch == 0) return MLA_OK;
   if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_units))
-    return hip_status(launch_combine_fast_balanced(d, c, n_units, o_part, lse_part, z, lse, (hipStream_t)stream));
-  return hip_status(launch_combine_generic_balanced(d, c, n_units, o_part, lse_part, z, lse, (hipStream_t)stream));
+    return hip_status(launch_combine_fast_balanced(d, c, n_units, p.o, p.lse, z, lse, (hipStream_t)stream));
+  return hip_status(launch_combine_generic_balanced(d, c, n_units, p.o, p.lse, z, lse, (hipStream_t)stream));
 }
 
 mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,
@@ -341,7 +396,7 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
   if (rows == 0) return MLA_OK;
   if (mfma) {
     MLA_TRY(ptr_ok(workspace));
-    if (workspace_bytes < kv_append_mfma_workspace(d_model, rows)) return MLA_ERR_SHAPE;
+    if (workspace_bytes < kv_append_mfma_workspace(d_model, rows)) return MLA_ERR_WORKSPACE;
     return hip_status(launch_kv_append_mfma(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps,
                                             workspace, (hipStream_t)stream, cache_fp8(dims)));
   }
@@ -399,7 +454,7 @@ mla_status mla_absorb_query_precomposed(const mla_dims* dims, int32_t d_cq, cons
   MLA_TRY(ptr_ok(q_hat));
   if (rows == 0) return MLA_OK;
   MLA_TRY(ptr_ok(workspace));
-  if (workspace_bytes < absorb_precomposed_workspace(d, d_cq, rows)) return MLA_ERR_SHAPE;
+  if (workspace_bytes < absorb_precomposed_workspace(d, d_cq, rows)) return MLA_ERR_WORKSPACE;
   return hip_status(launch_absorb_precomposed(d, d_cq, c_q, w_qcat, pos, rows, q_hat, workspace, (hipStream_t)stream));
 }
 
@@ -421,7 +476,7 @@ mla_status mla_out_proj_fused(const mla_dims* dims, int32_t d_model, const float
   MLA_TRY(ptr_ok(out));
   if (rows == 0) return MLA_OK;
   MLA_TRY(ptr_ok(workspace));
-  if (workspace_bytes < out_fused_workspace(d, d_model, rows)) return MLA_ERR_SHAPE;
+  if (workspace_bytes < out_fused_workspace(d, d_model, rows)) return MLA_ERR_WORKSPACE;
   return hip_status(launch_out_fused(d, d_model, z, w_uvo, rows, out, workspace, (hipStream_t)stream));
 }
 
@@ -444,7 +499,7 @@ mla_status mla_output_projection(const mla_dims* dims, int32_t d_model, const fl
   MLA_TRY(ptr_ok(out));
   if (rows == 0) return MLA_OK;
   MLA_TRY(ptr_ok(workspace));
-  if (workspace_bytes < output_projection_workspace(d, d_model, rows)) return MLA_ERR_SHAPE;
+  if (workspace_bytes < output_projection_workspace(d, d_model, rows)) return MLA_ERR_WORKSPACE;
   return hip_status(launch_output_projection(d, d_model, o, w_o, rows, out, workspace, (hipStream_t)stream));
 }
 

@@ -51,6 +51,19 @@ def balanced_units(lens, n_cu: int, min_tiles: int = 4) -> int:
     return max(1, min(int(n_cu), L.MLA_BALANCED_MAX_UNITS, -(-tiles // min_tiles)))
 
 
+def partials_workspace(d: L.MlaDims, slots: int, device, nbytes: int | None = None):
+    """A split-K workspace of `slots` partial slots (or `nbytes` bytes) and its two views:
+    o_part float [slots, H, d_c] and lse_part float [slots, H] (the layout of include/mla.h)."""
+    need = L.mla_partials_bytes(d, slots)
+    nbytes = need if nbytes is None else int(nbytes)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    off = L.mla_partials_lse_offset(d, slots)
+    H, dc = d.n_heads, d.d_c
+    o_part = ws[:slots * H * dc * 4].view(torch.float32).view(slots, H, dc)
+    lse_part = ws[off:off + slots * H * 4].view(torch.float32).view(slots, H)
+    return ws, nbytes, o_part, lse_part
+
+
 def dims_for(w, flags: int = 0) -> L.MlaDims:
     return L.dims(w.n_heads, w.d_c, w.d_r, w.d_k, w.d_v, dtype=L.MLA_BF16 if w.dtype == "bf16" else L.MLA_F32,
                   rope_base=w.rope_base, sm_scale=0.0, flags=flags)
@@ -85,15 +98,18 @@ class DecodeStep:
         if self.n_units is not None:
             self.split_tokens = 0
             self.S = L.mla_balanced_num_slots(self.B, self.n_units)
-            part_shape = (max(self.S, 1),)
+            slots = self.S
         else:
             self.split_tokens = int(split_tokens)
             self.S = L.mla_decode_num_splits(self.max_len, self.split_tokens)
-            part_shape = (self.B, self.S)
+            slots = self.B * self.S
         td = _torch_dtype(w.dtype)
         self.q_hat = torch.empty((self.B, H, W), dtype=td, device=dev)
-        self.o_part = torch.empty(part_shape + (H, w.d_c), dtype=torch.float32, device=dev)
-        self.lse_part = torch.empty(part_shape + (H,), dtype=torch.float32, device=dev)
+        self.ws, self.ws_bytes, o_part, lse_part = partials_workspace(self.d, slots, dev)
+        if self.n_units is None:  # slot b * S + i: chunk i of sequence b
+            o_part = o_part.view(self.B, self.S, H, w.d_c)
+            lse_part = lse_part.view(self.B, self.S, H)
+        self.o_part, self.lse_part = o_part, lse_part
         self.z = torch.empty((self.B, H, w.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.B, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, H, w.d_v), dtype=torch.float32, device=dev)
@@ -107,18 +123,16 @@ class DecodeStep:
 
     def attend(self, stream=None):
         if self.n_units is not None:
-            L.mla_decode_partial_balanced(self.d, self.c, self.q_hat, self.n_units, self.o_part, self.lse_part,
-                                          stream)
+            L.mla_decode_partial_balanced(self.d, self.c, self.q_hat, self.n_units, self.ws, self.ws_bytes, stream)
         else:
-            L.mla_decode_partial(self.d, self.c, self.q_hat, self.max_len, self.split_tokens, self.o_part,
-                                 self.lse_part, stream)
+            L.mla_decode_partial(self.d, self.c, self.q_hat, self.max_len, self.split_tokens, self.ws, self.ws_bytes,
+                                 stream)
 
     def combine(self, stream=None):
         if self.n_units is not None:
-            L.mla_combine_balanced(self.d, self.c, self.n_units, self.o_part, self.lse_part, self.z, self.lse,
-                                   stream)
+            L.mla_combine_balanced(self.d, self.c, self.n_units, self.ws, self.ws_bytes, self.z, self.lse, stream)
         else:
-            L.mla_combine(self.d, self.B, self.S, self.o_part, self.lse_part, self.z, self.lse, stream)
+            L.mla_combine(self.d, self.B, self.S, self.ws, self.ws_bytes, self.z, self.lse, stream)
 
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B, self.out, stream)
@@ -208,8 +222,7 @@ class VerifyStep:
         self.S = L.mla_balanced_num_slots(R, self.n_units)
         td = _torch_dtype(w.dtype)
         self.q_hat = torch.empty((R, H, W), dtype=td, device=dev)
-        self.o_part = torch.empty((max(self.S, 1), H, w.d_c), dtype=torch.float32, device=dev)
-        self.lse_part = torch.empty((max(self.S, 1), H), dtype=torch.float32, device=dev)
+        self.ws, self.ws_bytes, self.o_part, self.lse_part = partials_workspace(self.d, self.S, dev)
         self.z = torch.empty((self.B, self.Sq, H, w.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
@@ -224,10 +237,10 @@ class VerifyStep:
         L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.row_pos, self.B * self.Sq, self.q_hat, stream)
 
     def attend(self, stream=None):
-        L.mla_decode_partial_balanced(self.d, self.rc, self.q_hat, self.n_units, self.o_part, self.lse_part, stream)
+        L.mla_decode_partial_balanced(self.d, self.rc, self.q_hat, self.n_units, self.ws, self.ws_bytes, stream)
 
     def combine(self, stream=None):
-        L.mla_combine_balanced(self.d, self.rc, self.n_units, self.o_part, self.lse_part, self.z, self.lse, stream)
+        L.mla_combine_balanced(self.d, self.rc, self.n_units, self.ws, self.ws_bytes, self.z, self.lse, stream)
 
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B * self.Sq, self.out, stream)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings_and_splits():
-    for s in range(7):
+    for s in range(8):
         assert M.mla_status_str(s).startswith("MLA_")
     assert M.mla_decode_num_splits(131072, 512) == 256
     assert M.mla_decode_num_splits(4096, 256) == 16
@@ -70,9 +70,12 @@ def _absorb(d, q_c=A, q_r=A, w=A, pos=A, rows=1, q_hat=B_):
     return _status("mla_absorb_query", ctypes.byref(d) if d is not None else None, q_c, q_r, w, pos, rows, q_hat, None)
 
 
-def _decode(d, c, q_hat=A, max_len=131072, split=512, o=B_, lse=B_):
+BIG = 1 << 40  # a workspace size that passes every size check
+
+
+def _decode(d, c, q_hat=A, max_len=131072, split=512, ws=B_, nbytes=BIG):
     return _status("mla_decode_partial", ctypes.byref(d), ctypes.byref(c) if c is not None else None, q_hat,
-                   max_len, split, o, lse, None)
+                   max_len, split, ws, nbytes, None)
 
 
 def test_absorb_validation():
@@ -102,8 +105,8 @@ def test_decode_validation():
     assert _decode(d, _cache(), split=0) == M.MLA_ERR_SHAPE
     assert _decode(d, _cache(), max_len=2048 * 64 + 1) == M.MLA_ERR_SHAPE  # beyond the page table
     assert _decode(d, _cache(), max_len=-1) == M.MLA_ERR_SHAPE
-    assert _decode(d, _cache(), o=U) == M.MLA_ERR_ALIGN
-    assert _decode(d, _cache(), lse=None) == M.MLA_ERR_NULL
+    assert _decode(d, _cache(), ws=U) == M.MLA_ERR_ALIGN
+    assert _decode(d, _cache(), ws=None) == M.MLA_ERR_NULL
     assert _decode(d, _cache(batch=0)) == M.MLA_OK               # empty batch
     assert _decode(d, _cache(batch=70000)) == M.MLA_ERR_UNSUPPORTED
 
@@ -112,10 +115,11 @@ def test_other_entry_points_validation():
     lib = M.library()
     d = _dims()
     c = _cache()
-    assert lib.mla_combine(ctypes.byref(d), 4, 0, A, A, A, None, None) == M.MLA_ERR_SHAPE
-    assert lib.mla_combine(ctypes.byref(d), 4, 256, A, A, None, None, None) == M.MLA_ERR_NULL
-    assert lib.mla_combine(ctypes.byref(d), 4, 256, A, A, A, U, None) == M.MLA_ERR_ALIGN
-    assert lib.mla_combine(ctypes.byref(d), 0, 256, A, A, A, None, None) == M.MLA_OK
+    assert lib.mla_combine(ctypes.byref(d), 4, 0, A, BIG, A, None, None) == M.MLA_ERR_SHAPE
+    assert lib.mla_combine(ctypes.byref(d), 4, 256, A, BIG, None, None, None) == M.MLA_ERR_NULL
+    assert lib.mla_combine(ctypes.byref(d), 4, 256, A, BIG, A, U, None) == M.MLA_ERR_ALIGN
+    assert lib.mla_combine(ctypes.byref(d), 4, 256, None, BIG, A, None, None) == M.MLA_ERR_NULL
+    assert lib.mla_combine(ctypes.byref(d), 0, 256, A, 0, A, None, None) == M.MLA_OK
     assert lib.mla_out_proj(ctypes.byref(d), A, None, 4, A, None) == M.MLA_ERR_NULL
     assert lib.mla_out_proj(ctypes.byref(d), A, A, -2, A, None) == M.MLA_ERR_SHAPE
     assert lib.mla_out_proj(ctypes.byref(d), A, A, 0, A, None) == M.MLA_OK
@@ -145,16 +149,16 @@ def test_balanced_validation():
     assert M.mla_balanced_num_slots(4, 0) == -1
     assert M.mla_balanced_num_slots(4, M.MLA_BALANCED_MAX_UNITS + 1) == -1
 
-    def dec(c, n=256, q=A, o=B_, lse=B_):
-        return lib.mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), q, n, o, lse, None)
+    def dec(c, n=256, q=A, ws=B_, nbytes=BIG):
+        return lib.mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), q, n, ws, nbytes, None)
 
     def comb(c, n=256, z=A, lse=None):
-        return lib.mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n, A, A, z, lse, None)
+        return lib.mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n, A, BIG, z, lse, None)
 
     assert dec(_cache(), n=0) == M.MLA_ERR_SHAPE
     assert dec(_cache(), n=M.MLA_BALANCED_MAX_UNITS + 1) == M.MLA_ERR_UNSUPPORTED
     assert dec(_cache(), q=None) == M.MLA_ERR_NULL
-    assert dec(_cache(), o=U) == M.MLA_ERR_ALIGN
+    assert dec(_cache(), ws=U) == M.MLA_ERR_ALIGN
     assert dec(_cache(seq_lens=0)) == M.MLA_ERR_NULL
     assert dec(_cache(batch=0)) == M.MLA_OK
     # device-side cost sums must stay inside int32
@@ -182,7 +186,7 @@ def test_kv_append_workspace_validation():
                                  nbytes, None)
 
     assert call(ws=None) == M.MLA_ERR_NULL
-    assert call(nbytes=need - 4) == M.MLA_ERR_SHAPE
+    assert call(nbytes=need - 4) == M.MLA_ERR_WORKSPACE
     assert call(ws=U) == M.MLA_ERR_ALIGN
     assert call(rows=0, ws=None, nbytes=0) == M.MLA_OK
 
@@ -224,7 +228,7 @@ def test_fp8_flag_validation():
     c = _cache()
     for dd in (f8g, f8s):
         assert _decode(dd, c) == M.MLA_ERR_UNSUPPORTED
-        assert lib.mla_decode_partial_balanced(ctypes.byref(dd), ctypes.byref(c), A, 256, B_, B_,
+        assert lib.mla_decode_partial_balanced(ctypes.byref(dd), ctypes.byref(c), A, 256, B_, BIG,
                                                None) == M.MLA_ERR_UNSUPPORTED
         assert lib.mla_prefill_chunk(ctypes.byref(dd), ctypes.byref(c), A, 4, A, B_, None,
                                      None) == M.MLA_ERR_UNSUPPORTED
@@ -232,3 +236,39 @@ def test_fp8_flag_validation():
     assert lib.mla_decompress_kv(ctypes.byref(f8), ctypes.byref(c), 64, A, A, B_, B_, B_, None) == M.MLA_ERR_UNSUPPORTED
     assert lib.mla_kv_append(ctypes.byref(_dims(flags=M.MLA_FLAG_CACHE_FP8 | M.MLA_FLAG_FORCE_GENERIC)),
                              ctypes.byref(c), 4096, A, A, A, A, A, 4, 1e-6, A, 1 << 20, None) == M.MLA_ERR_UNSUPPORTED
+
+
+def test_split_k_workspace_sizes_and_rejection():
+    """The split-K workspace: its advertised size is the partials' closed form (o_part float
+    [slots, H, d_c], then lse_part float [slots, H] at a 256-byte boundary), and every decode or
+    combine call given one byte less returns MLA_ERR_WORKSPACE before anything is launched."""
+    lib = M.library()
+    d = _dims()
+    H, dc = 128, 512
+
+    def closed(slots):
+        o = slots * H * dc * 4
+        return -(-o // 256) * 256 + slots * H * 4
+
+    assert M.mla_partials_bytes(d, 3) == closed(3)
+    assert M.mla_partials_lse_offset(d, 3) == 3 * H * dc * 4
+    odd = _dims(n_heads=3, d_c=5)
+    assert M.mla_partials_lse_offset(odd, 1) == 256 and M.mla_partials_bytes(odd, 1) == 256 + 12
+    assert M.mla_partials_bytes(d, -1) == 0
+    c = _cache()  # batch 4
+    need = M.mla_decode_workspace_bytes(d, c, 131072, 512)
+    assert need == closed(4 * 256)
+    assert M.mla_decode_workspace_bytes(d, c, 131072, 0) == 0
+    assert M.mla_decode_workspace_bytes(d, c, 4097, 256) == closed(4 * 17)
+    need_b = M.mla_decode_balanced_workspace_bytes(d, c, 256)
+    assert need_b == closed(256 + 4 - 1)
+    assert M.mla_decode_balanced_workspace_bytes(d, c, 0) == 0
+    assert _decode(d, c, nbytes=need - 1) == M.MLA_ERR_WORKSPACE
+    assert lib.mla_combine(ctypes.byref(d), 4, 256, A, need - 1, A, None, None) == M.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_partial_balanced(ctypes.byref(d), ctypes.byref(c), A, 256, A, need_b - 1,
+                                           None) == M.MLA_ERR_WORKSPACE
+    assert lib.mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), 256, A, need_b - 1, A, None,
+                                    None) == M.MLA_ERR_WORKSPACE
+    # an empty batch needs no partial bytes
+    assert _decode(d, _cache(batch=0), nbytes=0) == M.MLA_OK
+    assert M.mla_decode_balanced_workspace_bytes(d, _cache(batch=0), 256) == 0

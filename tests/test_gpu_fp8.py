@@ -272,7 +272,7 @@ def test_fp8_unsupported_paths():
         M.mla_decompress_kv(d, c, 64, x, x, x, x, x)
     dg = runner.dims_for(w, F8 | M.MLA_FLAG_FORCE_GENERIC)
     with pytest.raises(M.MlaError):
-        M.mla_decode_partial_balanced(dg, c, x, 4, x, x)
+        M.mla_decode_partial_balanced(dg, c, x, 4, x, 64)
 
 
 @pytest.mark.parametrize("mode", ["fixed_8192", "balanced_2"])

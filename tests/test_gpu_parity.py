@@ -54,12 +54,13 @@ def test_toy_single_step_end_to_end(page_size, split):
     q_hat = torch.empty((1, w.n_heads, w.d_c + w.d_r), device=DEV)
     M.mla_absorb_query(d, q_c, q_r, dev(t["w_uk"]), dev(np.array([Lc - 1], np.int32)), 1, q_hat)
     S = M.mla_decode_num_splits(Lc, split)
-    o_part = torch.empty((1, S, w.n_heads, w.d_c), device=DEV)
-    lse_part = torch.empty((1, S, w.n_heads), device=DEV)
-    M.mla_decode_partial(d, c, q_hat, Lc, split, o_part, lse_part)
+    assert M.mla_decode_workspace_bytes(d, c, Lc, split) == M.mla_partials_bytes(d, S)
+    ws, ws_bytes, o_part, lse_part = runner.partials_workspace(d, S, DEV)
+    o_part, lse_part = o_part.view(1, S, w.n_heads, w.d_c), lse_part.view(1, S, w.n_heads)
+    M.mla_decode_partial(d, c, q_hat, Lc, split, ws, ws_bytes)
     z = torch.empty((1, w.n_heads, w.d_c), device=DEV)
     lse = torch.empty((1, w.n_heads), device=DEV)
-    M.mla_combine(d, 1, S, o_part, lse_part, z, lse)
+    M.mla_combine(d, 1, S, ws, ws_bytes, z, lse)
     out = torch.empty((1, w.n_heads, w.d_v), device=DEV)
     M.mla_out_proj(d, z, dev(t["w_uv"]), 1, out)
     torch.cuda.synchronize()
