@@ -23,6 +23,11 @@
  *   - Tensors are dense row-major in the index order written next to them.
  *   - Values of type "dtype" are float32 (MLA_F32) or bfloat16 bit patterns (MLA_BF16) as
  *     selected by mla_dims.dtype; arithmetic accumulates in float32.
+ *   - The absorbed query q_hat is float32 for MLA_F32 and IEEE binary16 for MLA_BF16: the score
+ *     products run in binary16 on the bf16 path (the bf16 cache values convert to binary16
+ *     exactly over the latents' range), whose 11 significant bits keep the score error of a
+ *     576-long dot product well inside the bf16 output tolerance.  Its values must stay within
+ *     +-65504 (scores of that size are far outside any softmax's useful range).
  */
 #ifndef MLA_H
 #define MLA_H
@@ -74,7 +79,7 @@ typedef struct {
   int32_t d_v;      /* value width per head */
   float rope_base;  /* RoPE base; inverse frequencies base^(-2i/d_r) on interleaved pairs */
   float sm_scale;   /* softmax scale; 0 selects 1/sqrt(d_k + d_r) ([ase] scale remark, Fig. 2) */
-  int32_t dtype;    /* mla_dtype of queries, weights, cache rows and q_hat */
+  int32_t dtype;    /* mla_dtype of queries, weights and cache rows (q_hat: see above) */
   int32_t flags;    /* MLA_FLAG_* */
 } mla_dims;
 
@@ -102,7 +107,7 @@ const char* mla_status_str(mla_status s);
  *   q_r   device dtype [rows, H, d_r]   (unrotated; may be NULL when d_r == 0)
  *   w_uk  device dtype [H, d_c, d_k]
  *   pos   device int32 [rows]           absolute position of each query row
- *   q_hat device dtype [rows, H, d_c + d_r]  (output)                                          */
+ *   q_hat device [rows, H, d_c + d_r]  (output; float32, or binary16 for MLA_BF16)             */
 mla_status mla_absorb_query(const mla_dims* dims, const void* q_c, const void* q_r, const void* w_uk,
                             const int32_t* pos, int32_t rows, void* q_hat, void* stream);
 
@@ -218,7 +223,7 @@ mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, 
 /* Causal multi-query attention for a chunk of new tokens whose rows are already in the cache
  * ([ase] causal-mask remark after Fig. 2; [molayo] chunked prefill).  Query i of sequence b sits
  * at absolute position q_start[b] + i and reads tokens t <= q_start[b] + i, t < seq_lens[b].
- *   q_hat   device dtype [batch, q_len, H, d_c + d_r]
+ *   q_hat   device [batch, q_len, H, d_c + d_r]  (as written by mla_absorb_query)
  *   q_start device int32 [batch]
  *   z       device float [batch, q_len, H, d_c]   (output, normalised)
  *   lse     device float [batch, q_len, H] or NULL (output, natural log)                         */
@@ -284,9 +289,9 @@ mla_status mla_precompose_query(const mla_dims* dims, int32_t d_cq, const void* 
 mla_status mla_precompose_out(const mla_dims* dims, int32_t d_model, const void* w_uv, const void* w_o, void* w_uvo,
                               void* stream);
 /* The absorbed query straight from the query latent: q_hat[r, h, :] = [c_q[r] . W_absorbed[h] |
- * RoPE_pos[r](c_q[r] . W_QR[h])] * sm_scale * log2(e), rounded to bf16 once (the layout and
+ * RoPE_pos[r](c_q[r] . W_QR[h])] * sm_scale * log2(e), rounded to binary16 once (the layout and
  * scaling of mla_absorb_query).  c_q bf16 [rows, d_cq]; w_qcat from mla_precompose_query; pos
- * device int32 [rows]; q_hat bf16 [rows, H, d_c + d_r].  workspace: device float32 scratch of at
+ * device int32 [rows]; q_hat binary16 [rows, H, d_c + d_r].  workspace: device float32 scratch of at
  * least mla_absorb_query_precomposed_workspace_bytes bytes (caller-owned, overwritten; smaller:
  * MLA_ERR_WORKSPACE). */
 size_t mla_absorb_query_precomposed_workspace_bytes(const mla_dims* dims, int32_t d_cq, int32_t rows);

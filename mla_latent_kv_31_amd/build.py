@@ -29,6 +29,9 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # loops marked `#pragma unroll` are schedules whose steps index register arrays: unroll them
+    # fully even when they are long (the default size limit leaves a 72-step loop rolled)
+    "-mllvm", "-pragma-unroll-threshold=100000",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]

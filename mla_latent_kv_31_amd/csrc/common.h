@@ -33,6 +33,23 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// ---------------------------------------------------------------- IEEE binary16 storage
+// The absorbed query of the bf16 path is stored in binary16: 11 significant bits instead of bf16's
+// 8 keep the score error of a 576-long dot product well inside the bf16 output tolerance.
+struct f16_t {
+  uint16_t bits;
+};
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+// Round to nearest even; beyond +-65504 the result is +-inf.
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+template <> struct Elem<f16_t> {
+  static __device__ __forceinline__ float load(const f16_t* p, size_t i) { return f16_to_f32(p[i].bits); }
+  static __device__ __forceinline__ void store(f16_t* p, size_t i, float v) { p[i].bits = f32_to_f16(v); }
+};
+// Storage type of q_hat for a given storage type of the other tensors.
+template <typename T> struct QHatOf { using type = T; };
+template <> struct QHatOf<uint16_t> { using type = f16_t; };
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

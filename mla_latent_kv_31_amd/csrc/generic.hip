@@ -20,31 +20,31 @@ constexpr int kThreads = 256;
 
 // -------------------------------------------------------------------------------- absorb
 // One block per (query row, head).  q_hat = [q_c . W_UK[h]^T | RoPE_pos(q_r)] * qscale.
-template <typename T>
+template <typename T, typename Q = typename QHatOf<T>::type>
 __global__ __launch_bounds__(kThreads) void absorb_generic_kernel(Dims d, const T* __restrict__ q_c,
                                                                   const T* __restrict__ q_r,
                                                                   const T* __restrict__ w_uk,
                                                                   const int32_t* __restrict__ pos,
-                                                                  T* __restrict__ q_hat, float qscale) {
+                                                                  Q* __restrict__ q_hat, float qscale) {
   extern __shared__ float qs[];  // [d_k]
   const int r = blockIdx.x, h = blockIdx.y;
   const size_t qi = size_t(r) * d.H + h;
   for (int k = threadIdx.x; k < d.dk; k += blockDim.x) qs[k] = Elem<T>::load(q_c, qi * d.dk + k);
   __syncthreads();
   const T* w = w_uk + size_t(h) * d.dc * d.dk;
-  T* out = q_hat + qi * d.W();
+  Q* out = q_hat + qi * d.W();
   for (int j = threadIdx.x; j < d.dc; j += blockDim.x) {
     float acc = 0.f;
     for (int k = 0; k < d.dk; ++k) acc = fmaf(qs[k], Elem<T>::load(w, size_t(j) * d.dk + k), acc);
-    Elem<T>::store(out, j, acc * qscale);
+    Elem<Q>::store(out, j, acc * qscale);
   }
   const double p = double(pos[r]);
   for (int i = threadIdx.x; i < d.dr / 2; i += blockDim.x) {
     const double ang = p * pow(double(d.rope_base), -2.0 * i / d.dr);
     const double cs = cos(ang), sn = sin(ang);
     const double x1 = Elem<T>::load(q_r, qi * d.dr + 2 * i), x2 = Elem<T>::load(q_r, qi * d.dr + 2 * i + 1);
-    Elem<T>::store(out, d.dc + 2 * i, float(x1 * cs - x2 * sn) * qscale);
-    Elem<T>::store(out, d.dc + 2 * i + 1, float(x1 * sn + x2 * cs) * qscale);
+    Elem<Q>::store(out, d.dc + 2 * i, float(x1 * cs - x2 * sn) * qscale);
+    Elem<Q>::store(out, d.dc + 2 * i + 1, float(x1 * sn + x2 * cs) * qscale);
   }
 }
 
@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kThreads) void absorb_generic_kernel(Dims d, const 
 // MODE kBalanced: blockIdx.x is a unit of the balanced split (schedule.h); a block whose segment
 // is empty writes nothing.
 enum { kFixed = 0, kPrefill = 1, kBalanced = 2 };
-template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache c, const T* __restrict__ q_hat,
+template <typename T, int MODE, typename Q = typename QHatOf<T>::type>
+__global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache c, const Q* __restrict__ q_hat,
                                                                   int split_tokens, int n_splits, int q_len,
                                                                   const int32_t* __restrict__ q_start,
                                                                   float* __restrict__ o_out,
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache 
     qrow = size_t(b) * d.H + h;
     orow = (size_t(b) * n_splits + x) * d.H + h;
   }
-  for (int k = threadIdx.x; k < W; k += blockDim.x) qs[k] = Elem<T>::load(q_hat, qrow * W + k);
+  for (int k = threadIdx.x; k < W; k += blockDim.x) qs[k] = Elem<Q>::load(q_hat, qrow * W + k);
   __syncthreads();
   const T* pool = static_cast<const T*>(c.pool);
   float acc[kGenericMaxDc / kThreads];
@@ -304,7 +304,7 @@ hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r
   const size_t shm = sizeof(float) * d.dk;
   if (d.dtype == MLA_BF16)
     absorb_generic_kernel<uint16_t><<<grid, kThreads, shm, s>>>(
-        d, (const uint16_t*)q_c, (const uint16_t*)q_r, (const uint16_t*)w_uk, pos, (uint16_t*)q_hat, q_scale(d));
+        d, (const uint16_t*)q_c, (const uint16_t*)q_r, (const uint16_t*)w_uk, pos, (f16_t*)q_hat, q_scale(d));
   else
     absorb_generic_kernel<float><<<grid, kThreads, shm, s>>>(d, (const float*)q_c, (const float*)q_r,
                                                              (const float*)w_uk, pos, (float*)q_hat, q_scale(d));
@@ -316,7 +316,7 @@ hipError_t launch_decode_generic(const Dims& d, const Cache& c, const void* q_ha
   const dim3 grid(n_splits, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, kFixed><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, split_tokens,
+    attend_generic_kernel<uint16_t, kFixed><<<grid, kThreads, shm, s>>>(d, c, (const f16_t*)q_hat, split_tokens,
                                                                        n_splits, 1, nullptr, o_part, lse_part);
   else
     attend_generic_kernel<float, kFixed><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, split_tokens, n_splits,
@@ -329,7 +329,7 @@ hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_h
   const dim3 grid(q_len, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, kPrefill><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, 0, 1, q_len,
+    attend_generic_kernel<uint16_t, kPrefill><<<grid, kThreads, shm, s>>>(d, c, (const f16_t*)q_hat, 0, 1, q_len,
                                                                       q_start, z, lse);
   else
     attend_generic_kernel<float, kPrefill><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, 1, q_len, q_start,
@@ -349,7 +349,7 @@ hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const v
   const dim3 grid(n_units, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const uint16_t*)q_hat, 0, n_units, 1,
+    attend_generic_kernel<uint16_t, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const f16_t*)q_hat, 0, n_units, 1,
                                                                           nullptr, o_part, lse_part);
   else
     attend_generic_kernel<float, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, n_units, 1,

@@ -5,7 +5,7 @@
 // multiplying consecutive projections ahead of time): the weight w_qcat [d_cq, H, d_c + d_r] holds,
 // for every head, [W_UQ[h] . W_UK[h]^T | W_QR[h]], so that one product c^Q . w_qcat gives every
 // head's latent-space query and unrotated rotary query at once; an epilogue rotates the rotary part
-// at the query position, applies sm_scale * log2(e) and rounds q_hat to bf16.
+// at the query position, applies sm_scale * log2(e) and rounds q_hat to binary16.
 //
 // Value side ([ase] same section, value side; [huny] section 2, output-projection fusion): the
 // weight w_uvo [H, d_c, d_model] holds W_UV[h] . W_O[h], so the layer output is
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
 }
 
 // Query epilogue: q_hat[r, h, :] = [sum_s part[s, r, h, 0:d_c] | RoPE_pos(sum_s part[s, r, h, d_c:])] *
-// qscale, rounded to bf16.  One wave per (row, head); lane l holds columns 8l..8l+7 of the 512
+// qscale, rounded to binary16 (the q_hat format of the bf16 path).  One wave per (row, head); lane l holds columns 8l..8l+7 of the 512
 // latent columns and, for l < 32, rotary pair l.
 struct RopeFreqP {
   double v[32];
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void query_epilogue_kernel(const float* __rest
   u32x4 w;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    w[q] = uint32_t(f32_to_bf16(v[2 * q] * qscale)) | (uint32_t(f32_to_bf16(v[2 * q + 1] * qscale)) << 16);
+    w[q] = uint32_t(f32_to_f16(v[2 * q] * qscale)) | (uint32_t(f32_to_f16(v[2 * q + 1] * qscale)) << 16);
   *reinterpret_cast<u32x4*>(o + 8 * lane) = w;
   if (lane < 32) {
     // angle pos * base^(-2i/d_r) in double, reduced to [-pi, pi] before the float sine and cosine
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void query_epilogue_kernel(const float* __rest
     float sn, cs;
     sincosf(float(rd), &sn, &cs);
     const float r1 = (x1 * cs - x2 * sn) * qscale, r2 = (x1 * sn + x2 * cs) * qscale;
-    *reinterpret_cast<uint32_t*>(o + 512 + 2 * lane) = uint32_t(f32_to_bf16(r1)) | (uint32_t(f32_to_bf16(r2)) << 16);
+    *reinterpret_cast<uint32_t*>(o + 512 + 2 * lane) = uint32_t(f32_to_f16(r1)) | (uint32_t(f32_to_f16(r2)) << 16);
   }
 }
 

@@ -3,9 +3,9 @@
 // mla_absorb_query ([ase] "Key 투영을 Query 쪽으로 옮기기", Fig. 3 equation):
 //   q_hat[r,h,j] = (sum_k q_c[r,h,k] W_UK[h,j,k]) * qscale,  j < d_c
 //   q_hat[r,h,d_c+2i, d_c+2i+1] = rotation of (q_r[r,h,2i], q_r[r,h,2i+1]) by pos[r]*base^(-2i/d_r), * qscale
-// computed transposed, q_hat^T = W_UK[h] . q_c^T, so that W_UK rows (contiguous over k) are the
-// A operand and query rows (contiguous over k) the B operand, both straight from global memory,
-// and the output tile is assembled in LDS and written as whole rows.  One workgroup per (head, 64
+// (q_hat stored in IEEE binary16), computed transposed, q_hat^T = W_UK[h] . q_c^T, so that W_UK
+// rows (contiguous over k) are the A operand and query rows (contiguous over k) the B operand, both
+// straight from global memory, and the output tile is assembled in LDS and written as whole rows.  One workgroup per (head, 64
 // query rows), all workgroups of a head on one XCD.
 //
 // mla_out_proj ([ase] "Value 투영을 가중합 뒤로 옮기기", Fig. 4 equation):
@@ -151,10 +151,10 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 v;
-        v[0] = uint32_t(f32_to_bf16(acc[rb][4 * g] * qscale)) |
-               (uint32_t(f32_to_bf16(acc[rb][4 * g + 1] * qscale)) << 16);
-        v[1] = uint32_t(f32_to_bf16(acc[rb][4 * g + 2] * qscale)) |
-               (uint32_t(f32_to_bf16(acc[rb][4 * g + 3] * qscale)) << 16);
+        v[0] = uint32_t(f32_to_f16(acc[rb][4 * g] * qscale)) |
+               (uint32_t(f32_to_f16(acc[rb][4 * g + 1] * qscale)) << 16);
+        v[1] = uint32_t(f32_to_f16(acc[rb][4 * g + 2] * qscale)) |
+               (uint32_t(f32_to_f16(acc[rb][4 * g + 3] * qscale)) << 16);
         *(lds_u32x2*)(trow + 8 * g) = v;
       }
     }
@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(int H, int R, int dr, 
       float sn, cs;
       sincosf(float(red), &sn, &cs);
       const float x1 = bf16_to_f32(uint16_t(in[k] & 0xffffu)), x2 = bf16_to_f32(uint16_t(in[k] >> 16));
-      outv[k] = uint32_t(f32_to_bf16((x1 * cs - x2 * sn) * qscale)) |
-                (uint32_t(f32_to_bf16((x1 * sn + x2 * cs) * qscale)) << 16);
+      outv[k] = uint32_t(f32_to_f16((x1 * cs - x2 * sn) * qscale)) |
+                (uint32_t(f32_to_f16((x1 * sn + x2 * cs) * qscale)) << 16);
     }
     *(lds_u32x4*)(tile + rr * TW + kDc + 8 * qd) = outv;
   }

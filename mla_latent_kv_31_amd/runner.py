@@ -38,6 +38,11 @@ def _torch_dtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
+def q_hat_dtype(dtype: str):
+    """Storage of the absorbed query: IEEE binary16 on the bf16 path, float32 otherwise."""
+    return torch.float16 if dtype == "bf16" else torch.float32
+
+
 def compute_units(device=None) -> int:
     """Compute units of the device (one balanced-split unit each)."""
     return int(torch.cuda.get_device_properties(torch.device(device or "cuda:0")).multi_processor_count)
@@ -104,7 +109,7 @@ class DecodeStep:
             self.S = L.mla_decode_num_splits(self.max_len, self.split_tokens)
             slots = self.B * self.S
         td = _torch_dtype(w.dtype)
-        self.q_hat = torch.empty((self.B, H, W), dtype=td, device=dev)
+        self.q_hat = torch.empty((self.B, H, W), dtype=q_hat_dtype(w.dtype), device=dev)
         self.ws, self.ws_bytes, o_part, lse_part = partials_workspace(self.d, slots, dev)
         if self.n_units is None:  # slot b * S + i: chunk i of sequence b
             o_part = o_part.view(self.B, self.S, H, w.d_c)
@@ -167,7 +172,7 @@ class PrefillStep:
         self.pos = to_device(pos, dev)
         H, W = w.n_heads, w.d_c + w.d_r
         td = _torch_dtype(w.dtype)
-        self.q_hat = torch.empty((self.B, self.Sq, H, W), dtype=td, device=dev)
+        self.q_hat = torch.empty((self.B, self.Sq, H, W), dtype=q_hat_dtype(w.dtype), device=dev)
         self.z = torch.empty((self.B, self.Sq, H, w.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, self.Sq, H, w.d_v), dtype=torch.float32, device=dev)
@@ -221,7 +226,7 @@ class VerifyStep:
         self.row_pos = torch.empty((R,), dtype=torch.int32, device=dev)
         self.S = L.mla_balanced_num_slots(R, self.n_units)
         td = _torch_dtype(w.dtype)
-        self.q_hat = torch.empty((R, H, W), dtype=td, device=dev)
+        self.q_hat = torch.empty((R, H, W), dtype=q_hat_dtype(w.dtype), device=dev)
         self.ws, self.ws_bytes, self.o_part, self.lse_part = partials_workspace(self.d, self.S, dev)
         self.z = torch.empty((self.B, self.Sq, H, w.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.B, self.Sq, H), dtype=torch.float32, device=dev)

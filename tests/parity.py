@@ -4,12 +4,13 @@ Tolerances:
   * the output of the path, o = z . W_UV:
       float32 inputs:             max |gpu - oracle| <= 1e-4 * RMS(oracle)
       bfloat16 inputs, fp32 acc:  max |gpu - oracle| <= 2e-2 * RMS(oracle)
-  * intermediates (the weighted latent z, split partials): the bf16 MFMA path rounds the
-    absorbed query and the softmax probabilities to bf16 (2^-9 relative each), which moves
-    single weights of a peaked softmax by a few 1e-3 before W_UV averages it over the latent
-    width.  Measured over many random sequences: relative RMS error ~2.2e-3, max/RMS up to
-    ~2.4e-2 for z.  Bound: max |err| <= 3e-2 * RMS and RMS(err) <= 5e-3 * RMS (bf16);
-    float32: 1e-4 and 1e-5.
+  * intermediates (the weighted latent z, split partials): the same bf16 bound on the largest
+    error, max |err| <= 2e-2 * RMS, and RMS(err) <= 5e-3 * RMS; float32: 1e-4 and 1e-5.  The bf16
+    path scores in IEEE binary16 (binary16 absorbed query times the exactly converted cache
+    values) and rounds the probabilities to binary16, 2^-11 relative each: a CPU simulation of
+    those roundings over short, peaked and long rows gives max/RMS of at most ~4e-3 on o and z
+    for every head of a row, against ~2.7e-2 when the query and the probabilities are rounded to
+    bf16.
   * lse (a log quantity) is compared in absolute terms: 2e-2 (bf16), 1e-4 (float32)
   * split-K indexing and length masking: exact (integer counts, bitwise re-runs)
 """
@@ -25,7 +26,7 @@ import oracle.mla_oracle as O
 from mla_workloads import gen
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-TOL_MID = {"f32": 1e-4, "bf16": 3e-2}
+TOL_MID = {"f32": 1e-4, "bf16": 2e-2}
 TOL_MID_RMS = {"f32": 1e-5, "bf16": 5e-3}
 
 
@@ -101,7 +102,7 @@ class OracleView:
         return O.absorbed_query(gen.as_f64(self.inp["q_c"][b], self.dt), gen.as_f64(self.inp["q_r"][b], self.dt),
                                 L - 1, self.w_uk, self.w.rope_base)
 
-    def prefill_row(self, b: int, i: int, heads) -> dict:
+    def prefill_row(self, b: int, i: int, heads=None) -> dict:
         q0 = int(self.inp["q_start"][b])
         cache = self.cache(b, q0 + i + 1)
         return O.attention(gen.as_f64(self.inp["q_c"][b, i], self.dt), gen.as_f64(self.inp["q_r"][b, i], self.dt),

@@ -150,9 +150,11 @@ def test_page_permutation_bitwise_and_determinism(flags):
 
 
 def test_split_invariance():
-    """Different chunkings agree within the bf16 tolerance: each chunk rounds P to bf16 relative
-    to its own running maximum, which moves single outputs by up to ~1% of the (small) RMS of z
-    when attention is peaked.  An indexing slip across chunk boundaries would be O(RMS)."""
+    """Different chunkings agree to rounding: each chunk rounds its probabilities to binary16
+    relative to its own reference maximum (2^-11 relative), and each result is within ~2e-3 of the
+    RMS of z of the exact one on short peaked rows (CPU simulation of those roundings), so two
+    splits differ by at most 4e-3 of it (measured: 1.7e-3 between 64-token chunks and whole
+    sequences).  An indexing slip across chunk boundaries would be O(RMS)."""
     lens = np.array([3000, 70, 4096], np.int32)
     note("split invariance")
     inp = gen.make_decode_inputs(_w(len(lens), seed=41), lens=lens)
@@ -161,7 +163,9 @@ def test_split_invariance():
         st = _run_partial(inp, split)
         zs.append((_np(st.z).copy(), _np(st.lse).copy()))
     for z, lse in zs[1:]:
-        assert np.max(np.abs(z - zs[0][0])) <= 2e-2 * np.sqrt(np.mean(zs[0][0] ** 2))
+        d = np.max(np.abs(z - zs[0][0])) / np.sqrt(np.mean(zs[0][0] ** 2))
+        note(f"split invariance: max |dz| / RMS(z) = {d:.2e}")
+        assert d <= 4e-3
         assert np.max(np.abs(lse - zs[0][1])) <= 1e-3
 
 
@@ -289,7 +293,9 @@ def test_balanced_matches_fixed_and_is_deterministic():
     for n_units in (1, 4, 33, 256):
         st = _run_balanced(inp, n_units)
         z, lse = _np(st.z).copy(), _np(st.lse).copy()
-        assert np.max(np.abs(z - z0)) <= 2e-2 * np.sqrt(np.mean(z0 ** 2)), n_units
+        d = np.max(np.abs(z - z0)) / np.sqrt(np.mean(z0 ** 2))
+        note(f"balanced vs fixed: n_units {n_units}, max |dz| / RMS(z) = {d:.2e}")
+        assert d <= 1e-3, n_units
         assert np.max(np.abs(lse - _np(ref.lse))) <= 1e-3
         st.attend()
         st.combine()
@@ -299,14 +305,15 @@ def test_balanced_matches_fixed_and_is_deterministic():
 
 # ------------------------------------------------------------------------------ prefill causal mask
 def _prefill_direct(inp, q_hat_np, q_start, flags=0):
-    """mla_prefill_chunk on a given q_hat [B, q_len, H, 576] (bf16 bits) and q_start [B]."""
+    """mla_prefill_chunk on a given q_hat [B, q_len, H, 576] (given as bf16 bits, stored as the
+    binary16 q_hat of the bf16 path: every test value is exact in both) and q_start [B]."""
     w = inp["workload"]
     d = runner.dims_for(w, flags)
     pool = runner.to_device(inp["pool"], DEV)
     table = runner.to_device(inp["page_table"], DEV)
     lens = runner.to_device(inp["lens"].astype(np.int32), DEV)
     c = M.cache(pool, table, lens)
-    qh = runner.to_device(q_hat_np, DEV)
+    qh = runner.to_device(q_hat_np, DEV).to(runner.q_hat_dtype(w.dtype))
     B, Sq = q_hat_np.shape[:2]
     z = torch.empty((B, Sq, 128, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((B, Sq, 128), dtype=torch.float32, device=DEV)

@@ -28,7 +28,6 @@ from parity import TOL, OracleView, assert_abs_close, assert_mid_close, assert_r
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 F8 = M.MLA_FLAG_CACHE_FP8
-HEADS = [0, 77, 127]
 
 
 def _np(t):
@@ -108,7 +107,7 @@ def _small_decode_inputs():
 
 @pytest.mark.parametrize("mode", ["balanced", "fixed"])
 def test_fp8_decode_small_ragged(mode):
-    """Lengths around the 32-token tile and the 64-token page, every sequence on three heads
+    """Lengths around the 32-token tile and the 64-token page, every head of every sequence
     against the oracle; every output bitwise against the bf16 decode of the dequantised pool."""
     inp = _small_decode_inputs()
     pool8 = oracle_fp8_pool(inp["pool"])
@@ -128,16 +127,16 @@ def test_fp8_decode_small_ragged(mode):
     view = Fp8View(inp8, pool8)
     tol = TOL["bf16"]
     for b in range(len(inp["lens"])):
-        ref = view.decode(b, heads=HEADS)
-        assert_mid_close(_np(st8.z)[b, HEADS], ref["z"][HEADS], "bf16", f"z seq {b}")
-        assert_abs_close(_np(st8.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
-        assert_rms_close(_np(st8.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
+        ref = view.decode(b)
+        assert_mid_close(_np(st8.z)[b], ref["z"], "bf16", f"z seq {b}")
+        assert_abs_close(_np(st8.lse)[b], ref["lse"], tol, f"lse seq {b}")
+        assert_rms_close(_np(st8.out)[b], ref["o"], tol, f"o seq {b}")
 
 
 def test_fp8_decode_v3_ragged_sampled():
     """The serving-scale batch (64 ragged sequences, 1k-32k tokens): the pool quantised on the GPU;
     for sampled sequences their rows equal the oracle's quantisation byte for byte, and the decode
-    matches the oracle over those rows (three heads)."""
+    matches the oracle over those rows (every head)."""
     inp = gen.make_decode_inputs(gen.WORKLOADS["v3_b64_ragged_paged"])
     P, ps, _ = inp["pool"].shape
     note("fp8 decode v3_b64_ragged_paged")
@@ -156,13 +155,13 @@ def test_fp8_decode_v3_ragged_sampled():
         codes, kr, scale = O.fp8_rows_unpack(mine)
         cache = np.concatenate([O.dequantize_latents_fp8(codes, scale), gen.as_f64(kr, "bf16")], axis=1)
         ref = O.attention(gen.as_f64(inp["q_c"][b], "bf16"), gen.as_f64(inp["q_r"][b], "bf16"), L - 1, cache,
-                          gen.as_f64(inp["w_uk"], "bf16"), gen.as_f64(inp["w_uv"], "bf16"), 512, heads=HEADS)
-        assert_abs_close(_np(st.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
-        assert_rms_close(_np(st.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
+                          gen.as_f64(inp["w_uk"], "bf16"), gen.as_f64(inp["w_uv"], "bf16"), 512)
+        assert_abs_close(_np(st.lse)[b], ref["lse"], tol, f"lse seq {b}")
+        assert_rms_close(_np(st.out)[b], ref["o"], tol, f"o seq {b}")
 
 
 def test_fp8_prefill_small():
-    """The chunked prefill over an FP8 pool: every row of a ragged-start chunk on three heads."""
+    """The chunked prefill over an FP8 pool: every head of every row of a ragged-start chunk."""
     w = gen.Workload(name="fp8_prefill", seed=73, kind="prefill", batch=3, ctx=70, q_len=24, random_pages=True)
     inp = gen.make_prefill_inputs(w)
     inp["q_start"] = np.array([70, 0, 13], np.int32)
@@ -176,14 +175,14 @@ def test_fp8_prefill_small():
     tol = TOL["bf16"]
     for b in range(3):
         for i in range(w.q_len):
-            ref = view.prefill_row(b, i, HEADS)
-            assert_abs_close(_np(st.lse)[b, i, HEADS], ref["lse"][HEADS], tol, f"lse ({b},{i})")
-            assert_rms_close(_np(st.out)[b, i, HEADS], ref["o"][HEADS], tol, f"o ({b},{i})")
+            ref = view.prefill_row(b, i)
+            assert_abs_close(_np(st.lse)[b, i], ref["lse"], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i], ref["o"], tol, f"o ({b},{i})")
 
 
 def test_fp8_verify_small():
-    """Multi-token verify over an FP8 pool (draft rows through the balanced decode): every row on
-    three heads against the oracle's prefill rows on the dequantised latents, and bitwise equal to
+    """Multi-token verify over an FP8 pool (draft rows through the balanced decode): every head of
+    every row against the oracle's prefill rows on the dequantised latents, and bitwise equal to
     the verify over the bf16 pool that holds those values."""
     w = gen.Workload(name="fp8_verify", seed=75, kind="prefill", batch=4, ctx_range=(1, 300), q_len=4,
                      random_pages=True)
@@ -198,9 +197,9 @@ def test_fp8_verify_small():
     tol = TOL["bf16"]
     for b in range(w.batch):
         for i in range(w.q_len):
-            ref = view.prefill_row(b, i, HEADS)
-            assert_abs_close(_np(st.lse)[b, i, HEADS], ref["lse"][HEADS], tol, f"lse ({b},{i})")
-            assert_rms_close(_np(st.out)[b, i, HEADS], ref["o"][HEADS], tol, f"o ({b},{i})")
+            ref = view.prefill_row(b, i)
+            assert_abs_close(_np(st.lse)[b, i], ref["lse"], tol, f"lse ({b},{i})")
+            assert_rms_close(_np(st.out)[b, i], ref["o"], tol, f"o ({b},{i})")
     sd = runner.VerifyStep(dict(inp, pool=dequantized_bf16_pool(pool8)), DEV, n_units=16)
     sd.run()
     torch.cuda.synchronize()
@@ -280,7 +279,7 @@ def test_fp8_decode_long_segments(mode):
     """Segments longer than 64 pages, so the kernel moves its page window inside a segment (the
     rotary rows of the next tile keep the address taken before the move): one 10,000-token and one
     5,000-token sequence, fixed 8,192-token chunks or two balanced units.  Bitwise against the bf16
-    decode of the dequantised pool, and against the oracle on three heads."""
+    decode of the dequantised pool, and against the oracle on every head."""
     w = gen.Workload(name="fp8_long", seed=76, kind="decode", batch=2, ctx_range=(1, 10000), random_pages=True)
     inp = gen.make_decode_inputs(w, lens=np.array([10000, 5000], np.int32))
     pool8 = oracle_fp8_pool(inp["pool"])
@@ -299,6 +298,6 @@ def test_fp8_decode_long_segments(mode):
     view = Fp8View(inp8, pool8)
     tol = TOL["bf16"]
     for b in range(2):
-        ref = view.decode(b, heads=HEADS)
-        assert_abs_close(_np(st8.lse)[b, HEADS], ref["lse"][HEADS], tol, f"lse seq {b}")
-        assert_rms_close(_np(st8.out)[b, HEADS], ref["o"][HEADS], tol, f"o seq {b}")
+        ref = view.decode(b)
+        assert_abs_close(_np(st8.lse)[b], ref["lse"], tol, f"lse seq {b}")
+        assert_rms_close(_np(st8.out)[b], ref["o"], tol, f"o seq {b}")
