@@ -499,7 +499,7 @@ def bench_precomposed(args, w) -> dict:
     wso = L.mla_out_proj_fused_workspace_bytes(d, dm, R)
     wsp = L.mla_output_projection_workspace_bytes(d, dm, R)
     ws = torch.empty(max(wsq, wso, wsp) // 4, dtype=torch.float32, device=dev)
-    q_hat = torch.empty((R, H, dc + dr), dtype=torch.bfloat16, device=dev)
+    q_hat = torch.empty((R, H, dc + dr), dtype=torch.float16, device=dev)
     out = torch.empty((R, dm), dtype=torch.float32, device=dev)
     q_c = torch.randn((R, H, dk), device=dev).to(torch.bfloat16)
     q_r = torch.randn((R, H, dr), device=dev).to(torch.bfloat16)
