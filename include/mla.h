@@ -356,6 +356,24 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
                          const int32_t* positions, int32_t rows, float rms_eps, float* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Allocation-free cache write, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): mla_kv_append with the
+ * split-K partial products in a fixed scratch array of MLA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends, instead of a caller workspace.  Arguments,
+ * results and errors are those of mla_kv_append; a call whose partial products would exceed the
+ * scratch (mla_kv_append_workspace_bytes(dims, d_model, rows) > MLA_NOALLOC_SCRATCH_BYTES, which
+ * holds exactly when rows > 3640, whatever d_model) returns MLA_ERR_WORKSPACE before anything is
+ * launched.  Shapes that take the generic kernel use no scratch and have no such limit.
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap on a GPU (concurrent
+ * streams, or threads without ordering between their streams) race and must not be issued.  The
+ * scratch needs no clearing (each call overwrites what it reads).  The first call on each device
+ * looks up the array's device address (no allocation); make one call before capturing a graph that
+ * contains this one. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+mla_status mla_kv_append_noalloc(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                                 const int32_t* positions, int32_t rows, float rms_eps, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ MLA_BF16 = 1
 MLA_FLAG_FORCE_GENERIC = 1
 MLA_FLAG_CACHE_FP8 = 2
 MLA_FP8_ROW_BYTES = 656
+MLA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # Balanced split-K constants (include/mla.h)
 MLA_BALANCED_TILE = 32
@@ -81,6 +82,7 @@ _SIGNATURES = {
     "mla_prefill_unabsorbed_supported": (_I32, [_PD]),
     "mla_kv_append_workspace_bytes": (ctypes.c_size_t, [_PD, _I32, _I32]),
     "mla_kv_append": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP, ctypes.c_size_t, _VP]),
+    "mla_kv_append_noalloc": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _F32, _VP]),
     "mla_verify_rows": (_I32, [_PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_quantize_rows_fp8": (_I32, [_PD, _VP, ctypes.c_int64, _VP, _VP]),
     "mla_precompose_query": (_I32, [_PD, _I32, _VP, _VP, _VP, _VP, _VP]),
@@ -318,3 +320,11 @@ def mla_kv_append(d: MlaDims, c: MlaCache, d_model: int, h, w_dkv, w_kr, seq_ids
                                    _addr(seq_ids), _addr(positions), rows, rms_eps, _addr(workspace),
                                    workspace_bytes, _stream(stream)),
            "mla_kv_append")
+
+
+def mla_kv_append_noalloc(d: MlaDims, c: MlaCache, d_model: int, h, w_dkv, w_kr, seq_ids, positions, rows: int,
+                          rms_eps: float = 0.0, stream=None) -> None:
+    _check(library().mla_kv_append_noalloc(ctypes.byref(d), ctypes.byref(c), d_model, _addr(h), _addr(w_dkv),
+                                           _addr(w_kr), _addr(seq_ids), _addr(positions), rows, rms_eps,
+                                           _stream(stream)),
+           "mla_kv_append_noalloc")

@@ -404,6 +404,35 @@ mla_status mla_kv_append(const mla_dims* dims, const mla_cache* cache, int32_t d
       launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
 }
 
+mla_status mla_kv_append_noalloc(const mla_dims* dims, const mla_cache* cache, int32_t d_model, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* seq_ids,
+                                 const int32_t* positions, int32_t rows, float rms_eps, void* stream) {
+  Dims d;
+  Cache c;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  if (d_model < 1 || rows < 0 || !(rms_eps == rms_eps)) return MLA_ERR_SHAPE;
+  const bool mfma = kv_append_uses_mfma(dims, d, d_model);
+  if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
+  if (!mfma && d_model + d.dc + d.dr > 8192) return MLA_ERR_UNSUPPORTED;
+  if (mfma && int64_t(rows) * d_model > (int64_t(1) << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(ptr_ok(h));
+  MLA_TRY(ptr_ok(w_dkv));
+  if (d.dr > 0) MLA_TRY(ptr_ok(w_kr));
+  MLA_TRY(ptr_ok(seq_ids));
+  MLA_TRY(ptr_ok(positions));
+  if (rows == 0) return MLA_OK;
+  if (mfma) {
+    if (kv_append_mfma_workspace(d_model, rows) > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+    float* scratch = nullptr;
+    MLA_TRY(hip_status(kv_append_noalloc_scratch(&scratch)));
+    return hip_status(launch_kv_append_mfma(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps,
+                                            scratch, (hipStream_t)stream, cache_fp8(dims)));
+  }
+  return hip_status(
+      launch_kv_append(d, c, d_model, h, w_dkv, w_kr, seq_ids, positions, rows, rms_eps, (hipStream_t)stream));
+}
+
 static bool precomposed_dims(const mla_dims* dims, Dims* d) {
   return check_dims(dims, d) == MLA_OK && precomposed_supported(*d);
 }

@@ -23,6 +23,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "fp8.h"
 #include "launch.h"
@@ -240,7 +242,34 @@ int kv_splits(int d_model, int rows) {
   return best;
 }
 
+// Scratch of the allocation-free cache write (mla_kv_append_noalloc): the split-K partial products
+// go to this file-scope device array instead of a caller workspace.  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code the array's name is only a stand-in:
+// kernels get the device address hipGetSymbolAddress returns for the current device, looked up on
+// the first call on each device and kept per device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t kv_append_noalloc_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(g_scratch_addr[dev]);
+  return hipSuccess;
+}
 
 bool kv_append_mfma_supported(const Dims& d, int d_model) {
   return d.dtype == MLA_BF16 && d.dc == kDc && d.dr == kDr && d_model >= kChunk && d_model % kChunk == 0;

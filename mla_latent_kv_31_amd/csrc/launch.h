@@ -83,6 +83,10 @@ size_t kv_append_mfma_workspace(int d_model, int rows);
 hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                                  const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                                  float rms_eps, float* workspace, hipStream_t s, bool fp8 = false);
+// The allocation-free variant's fixed scratch (kv_append_mfma.hip): its device address on the
+// current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+hipError_t kv_append_noalloc_scratch(float** ptr);
 hipError_t launch_kv_append(const Dims& d, const Cache& c, int d_model, const void* h, const void* w_dkv,
                             const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                             float rms_eps, hipStream_t s);

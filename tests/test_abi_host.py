@@ -191,6 +191,30 @@ def test_kv_append_workspace_validation():
     assert call(rows=0, ws=None, nbytes=0) == M.MLA_OK
 
 
+def test_kv_append_noalloc_validation():
+    """The allocation-free cache write refuses, before any launch, a call whose split-K partial
+    products would not fit its fixed scratch: rows > 3640 at any d_model (at most 1,820 rows take
+    more than one split, and one split of 3,641 rows of 576 floats exceeds 8 MiB)."""
+    lib = M.library()
+    d = _dims()
+    assert M.MLA_NOALLOC_SCRATCH_BYTES == 8 << 20
+
+    def call(rows, d_model=4096, dd=d, ptr=A):
+        return lib.mla_kv_append_noalloc(ctypes.byref(dd), ctypes.byref(_cache()), d_model, ptr, A, A, A, A, rows,
+                                         1e-6, None)
+
+    for dm in (4096, 7168, 16384):
+        for rows in (1, 64, 1024, 1821, 3640):
+            assert M.mla_kv_append_workspace_bytes(d, dm, rows) <= M.MLA_NOALLOC_SCRATCH_BYTES, (dm, rows)
+        assert M.mla_kv_append_workspace_bytes(d, dm, 3641) > M.MLA_NOALLOC_SCRATCH_BYTES
+        assert call(3641, dm) == M.MLA_ERR_WORKSPACE
+    assert call(0) == M.MLA_OK
+    assert call(-1) == M.MLA_ERR_SHAPE
+    assert call(64, ptr=None) == M.MLA_ERR_NULL
+    # fp8 rows need the MFMA path; f32 takes the generic kernel, which uses no scratch
+    assert call(64, d_model=4000, dd=_dims(flags=M.MLA_FLAG_CACHE_FP8)) == M.MLA_ERR_UNSUPPORTED
+
+
 def test_verify_rows_validation():
     lib = M.library()
     c = _cache()
