@@ -307,8 +307,17 @@ def attention_absorbed(q_c, q_r, q_pos, cache, w_uk, w_uv, d_c, scale=None, base
         a, lse[h] = softmax_lse(s[h])
         if keys.size:
             z[h] = a @ rows[:, :d_c]
-    o = np.einsum("hc,hcv->hv", z, w_uv)
+    o = absorbed_output(z, w_uv)
     return dict(o=o, z=z, lse=lse, s=s, keys=keys)
+
+
+def absorbed_output(z: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """o_h = z_h . W_UV[h] for every head: the value up-projection applied once to the weighted
+    latent instead of to every cached row ([ase] Fig. 4 equation; [huny] section 2, value
+    absorption).  z [..., H, d_c], w_uv [H, d_c, d_v] -> [..., H, d_v]."""
+    z = np.asarray(z, F64)
+    w_uv = np.asarray(w_uv, F64)
+    return np.einsum("...hc,hcv->...hv", z, w_uv)
 
 
 # --------------------------------------------------------------------------

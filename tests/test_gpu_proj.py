@@ -6,8 +6,9 @@ prefill steps use and at ragged counts around the 32- and 64-row workgroup tiles
         |gpu - oracle| <= 2^-11 |oracle| + 2^-24 + 1e-5 * RMS(oracle)
     (half a binary16 ulp, the binary16 subnormal spacing, and slack for the fp32 accumulation over
     128 products).
-  * mla_out_proj ([ase] Fig. 4 equation): out = z . W_UV[h] with float32 z and output.  z enters
-    the MFMAs as a bf16 hi + lo pair (about 16 significant bits), so the float32 bound applies:
+  * mla_out_proj ([ase] Fig. 4 equation): out = z . W_UV[h] with float32 z and output, against
+    oracle.absorbed_output.  z enters the MFMAs as a bf16 hi + lo pair (about 16 significant
+    bits), so the float32 bound applies:
         max |gpu - oracle| <= 1e-4 * RMS(oracle).
 Inputs: q_C, q_R, z ~ N(0,1); W_UK, W_UV ~ N(0,1)/sqrt(512), stored bf16; positions uniform on
 [0, 131072).
@@ -70,7 +71,7 @@ def test_out_proj_rows(rows):
     M.mla_out_proj(_dims(), runner.to_device(z, DEV), runner.to_device(w_uv, DEV), rows, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    ref = np.einsum("rhj,hjv->rhv", z.astype(np.float64), gen.as_f64(w_uv, "bf16"))
+    ref = O.absorbed_output(z.astype(np.float64), gen.as_f64(w_uv, "bf16"))
     rms = math.sqrt(float(np.mean(ref ** 2)))
     err = float(np.max(np.abs(got - ref)))
     assert err <= 1e-4 * rms, f"out_proj rows {rows}: max err {err:.3e} > 1e-4 * rms {rms:.3e}"
