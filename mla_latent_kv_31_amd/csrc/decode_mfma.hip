@@ -82,6 +82,7 @@ constexpr int kNBuf = 4;                         // LDS tile buffers
 constexpr int kTileB = kTile * kRowB;            // 36,864 bytes
 constexpr int kRopeOff = kTile * kLatB;          // rotary region offset inside a tile buffer
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;                         // accelerator complex dies, one L2 each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLatPerWave = kTile / kWaves;      // 8 latent-row transfers per wave per tile
 constexpr int kDmaPerWave = kLatPerWave + 1;     // + 1 rotary transfer (8 rotary rows)
@@ -123,12 +124,26 @@ static_assert(kLdsB8 <= 160 * 1024, "FP8 layout fits the CU's LDS");
 __host__ __device__ constexpr int lat_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __host__ __device__ constexpr int rope_swz(int row) { return (row >> 1) & 7; }
 
+// v_max_f32 / v_max3_f32 as such.  fmaxf would first quiet each operand with a v_max_f32 of the
+// value with itself (for signalling NaNs); the scores here come out of MFMAs, which never produce
+// one.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Max / sum over the four lanes l%16 + 16g (g = 0..3) that hold one head's scores.
 __device__ __forceinline__ float head_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float head_sum(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -148,6 +163,12 @@ __device__ __forceinline__ void score_mfma(bool first, f32x4& acc, const f16x8& 
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void score_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"); }
+
+// LDS byte address of a pointer into the kernel's one shared array, and back.  Tile buffers start
+// at multiples of 4 KiB, so a per-lane offset whose swizzle bits lie below 4 KiB can be XORed after
+// the buffer address is added.
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return uint32_t(reinterpret_cast<uintptr_t>(p)); }
+__device__ __forceinline__ lds_u8* lds_ptr(uint32_t a) { return reinterpret_cast<lds_u8*>(uintptr_t(a)); }
 
 __device__ __forceinline__ f16x8 lds16(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f16x8*>(p);
@@ -252,9 +273,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
   };
   // weighted-sum operand o = 8 * kstep + mb (mb: block of this wave's latent half): two
   // transposing reads, tokens 4(2h+s) + 0..3 and 16 + the same
-  auto tr8 = [&](const lds_u8* tb, int o) {
+  // pb: the tile buffer's address plus pv_x
+  auto tr8 = [&](uint32_t pb, int o) {
     const int s = o >> 3, mb = o & 7;
-    const lds_u8* p0 = tb + 4 * kLatB * s + 256 * (mb >> 2) + (pv_x ^ (64 * (mb & 3) + 16 * s));
+    const lds_u8* p0 = lds_ptr((pb ^ uint32_t(64 * (mb & 3) + 16 * s)) + 4 * kLatB * s + 256 * (mb >> 2));
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
     const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + 16 * kLatB));
     return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -264,8 +286,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     return x < kLatPerWave ? tbuf + (4 * x + wave_u) * kLatB + lane16 : tbuf + kRopeOff + wave_u * 1024 + lane16;
   };
 
-  // ---- the segment list
-  const int unit = blockIdx.x;
+  // ---- the segment list.  Workgroups are dealt to the chip's eight XCDs (each with its own L2) in
+  // turn, workgroup id modulo 8; consecutive units of the work-balanced split, which mostly share
+  // a sequence (and so its q_hat rows and page-table row), are placed on one XCD.
+  int unit = blockIdx.x;
+  if constexpr (kBal) {
+    if (gridDim.x % kXcds == 0) unit = (unit % kXcds) * (gridDim.x / kXcds) + unit / kXcds;
+  }
   int next_b, next_cb = 0, unit_end = 0, quota = 0;
   if constexpr (kBal) {
     int total;
@@ -543,7 +570,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
         // compiler hoist dozens of precomputed copies into registers next to the q_hat fragments.
         asm volatile("" : "+v"(qa_x), "+v"(qr_x), "+v"(pv_x), "+v"(lane16));
         lds_u8* const tb = lbase + (j % kNB) * kTileB;
-        lds_u8* const tp = lbase + ((j + kNB - 1) % kNB) * kTileB;
+        const uint32_t tp = lds_addr(lbase + ((j + kNB - 1) % kNB) * kTileB) + uint32_t(pv_x);
         lds_u8* const tn = lbase + ((j + 1) % kNB) * kTileB;
         const int nvalid = min(kTile, t1 - (t0 + j * kTile));
         const int nvalid_next = min(kTile, t1 - (t0 + (j + 1) * kTile));
@@ -641,11 +668,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
                 __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[o % (kPB + 1)], pp, acc[2 * (o & 7) + nb], 0, 0, 0);
             if (i == 1 || i == 2) {  // row maximum of head block i-1 over this lane's 8 tokens, then the head
               const int hb = i - 1;
-              float m = fmaxf(fmaxf(sacc[0][hb][0], sacc[0][hb][1]), fmaxf(sacc[0][hb][2], sacc[0][hb][3]));
-              m = fmaxf(m, fmaxf(fmaxf(sacc[1][hb][0], sacc[1][hb][1]), fmaxf(sacc[1][hb][2], sacc[1][hb][3])));
+              const f32x4 u = sacc[0][hb], v = sacc[1][hb];
+              const float m = vmax(vmax3(u[0], u[1], u[2]), vmax3(u[3], v[0], vmax3(v[1], v[2], v[3])));
               mx[hb] = head_max(m);
               m_ref[hb] = first ? mx[hb] : m_ref[hb];
-              m_max[hb] = fmaxf(m_max[hb], mx[hb]);
+              m_max[hb] = vmax(m_max[hb], mx[hb]);
               over |= mx[hb] > m_ref[hb] + kRerunMargin;
             }
             // one probability per step (the exp2 is a quarter-rate instruction), summed and packed
@@ -705,7 +732,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       {
-        lds_u8* const tp = lbase + ((ntiles - 1) % kNB) * kTileB;
+        const uint32_t tp = lds_addr(lbase + ((ntiles - 1) % kNB) * kTileB) + uint32_t(pv_x);
         const f16x8 pq0 = lds16(x_at(x_peer, (ntiles - 1) & 1, 0));
         const f16x8 pq1 = lds16(x_at(x_peer, (ntiles - 1) & 1, 1));
         f16x8 pa[3];
