@@ -39,6 +39,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kDc = 512, kDr = 64, kW = kDc + kDr;
+constexpr int kXcds = 8;  // accelerator complex dies, one L2 each
 constexpr int kCols = 32;             // output columns per workgroup
 constexpr int kColTiles = kW / kCols; // 18
 constexpr int kRowsWg = 64;           // output rows per workgroup (two waves)
@@ -139,6 +140,138 @@ __global__ __launch_bounds__(kThreads) void kv_gemm_kernel(const uint16_t* __res
   }
 }
 
+// kv_gemm_tiled_kernel, for 512 rows and more (prefill-sized writes), where reusing h and the weight
+// slice from LDS matters more than streaming the weights: a workgroup of four waves computes a
+// 64-row x 64-column tile over its K range, wave w rows 32(w&1).., columns 32(w>>1)...  Both
+// operands are staged per 64-k chunk with global_load_lds transfers, three chunks ahead of the one
+// multiplied (16 KiB per chunk: h rows and weight k-rows of 128 bytes each).  Workgroups are dealt to
+// the eight XCDs in turn; the tiles of one row tile (all column tiles and K splits, which share its
+// h rows) go to one XCD, so that they share its L2.  16-byte chunks of an h row are XOR-swizzled
+// by (row>>1)&7, so 16 consecutive rows at one logical chunk (an A-operand read) hit 16 distinct
+// bank groups; those of a weight k-row by 4((k>>1)&1), so the 4 k-rows x 64 bytes of a transposing
+// read do.  Each lane's transfer fetches the global piece the swizzle places at its position.
+constexpr int kTM = 64, kTN = 64, kKC = 64;                // tile rows, columns, k per chunk
+constexpr int kTThreads = 256, kTStages = 4;
+constexpr int kTRowB = kKC * 2;                            // 128 bytes per staged row
+constexpr int kTAB = kTM * kTRowB, kTBB = kKC * kTRowB;    // 8 KiB each
+constexpr int kTStageB = kTAB + kTBB;
+constexpr int kTColTiles = kW / kTN;                       // 9: eight of W_DKV, one of W_KR
+static_assert(kW % kTN == 0 && kDc % kTN == 0, "column tiles");
+
+__device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const void* gbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase)
+               : "memory");
+}
+
+__global__ __launch_bounds__(kTThreads) void kv_gemm_tiled_kernel(const uint16_t* __restrict__ h, int d_model,
+                                                                 int rows, const uint16_t* __restrict__ w_dkv,
+                                                                 const uint16_t* __restrict__ w_kr, int k_per_split,
+                                                                 float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kTStages * kTStageB];
+  lds_u8* const lbase = (lds_u8*)smem;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(lbase));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // workgroup id -> (column tile, row tile, split): XCD x = id % 8 takes row tiles x, x + 8, ...
+  const int n_rt = (rows + kTM - 1) / kTM, n_split = gridDim.x / (kTColTiles * n_rt);
+  int ct, rt, ks;
+  {
+    const int id = blockIdx.x;
+    if (n_rt % kXcds == 0) {
+      const int per = kTColTiles * n_split, slot = id / kXcds;
+      rt = id % kXcds + kXcds * (slot / per);
+      ct = (slot % per) % kTColTiles;
+      ks = (slot % per) / kTColTiles;
+    } else {
+      ct = id % kTColTiles;
+      rt = (id / kTColTiles) % n_rt;
+      ks = id / (kTColTiles * n_rt);
+    }
+  }
+  const int col0 = ct * kTN, row0 = rt * kTM;
+  const uint16_t* const wsrc = col0 < kDc ? w_dkv + col0 : w_kr + (col0 - kDc);
+  const int wstride = col0 < kDc ? kDc : kDr;
+  const int k_begin = ks * k_per_split, nchunks = k_per_split / kKC;
+
+  // transfers: wave w moves staged rows 8(2w+x) .. +7 (x = 0, 1) of h and of the weight slice; lane
+  // L writes 16 bytes at position L of that 1 KiB, i.e. row +L/8, physical chunk L%8
+  uint32_t a_voff[2], b_voff[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int r = 8 * (2 * wave + x) + (lane >> 3), p = lane & 7;
+    const int grow = min(row0 + r, rows - 1);  // rows past the end: a valid row, never stored
+    a_voff[x] = uint32_t((size_t(grow) * d_model + 8 * (p ^ ((r >> 1) & 7))) * 2);
+    b_voff[x] = uint32_t((r * wstride + 8 * (p ^ (4 * ((r >> 1) & 1)))) * 2);
+  }
+  auto issue = [&](int c) {  // chunk c into stage c % 3
+    const int k0 = k_begin + c * kKC;
+    const uint32_t st = lds0 + uint32_t((c % kTStages) * kTStageB);
+    const uint16_t* ga = h + k0;
+    const uint16_t* gb = wsrc + size_t(k0) * wstride;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      dma16(st + uint32_t(1024 * (2 * wave + x)), a_voff[x], ga);
+      dma16(st + uint32_t(kTAB + 1024 * (2 * wave + x)), b_voff[x], gb);
+    }
+  };
+
+  // operand reads.  A (32 rows x 16 k of k-step s): lane l reads row 32(w&1) + l%32, logical chunk
+  // 2s + l/32.  B (16 k x 32 columns): two transposing reads of 4 k-rows x 16 columns per 16-lane
+  // group; group g, lane i: k-rows 8(g/2) + i/4 (and +4) of the k-step, columns 32(w>>1) +
+  // 16(g%2) + 4(i%4) .. +3.
+  const int wm = wave & 1, wn = wave >> 1;
+  const int ar = 32 * wm + (lane & 31);
+  const uint32_t a_off = uint32_t(ar * kTRowB + 16 * ((lane >> 5) ^ ((ar >> 1) & 7)));
+  const int g = lane >> 4, i16 = lane & 15;
+  const int q = 4 * wn + 2 * (g & 1) + ((i16 & 3) >> 1);  // logical 16-byte chunk of the columns
+  const int kr0 = 8 * (g >> 1) + (i16 >> 2);
+  const uint32_t b_lo = uint32_t(kTAB + kr0 * kTRowB + 16 * (q ^ (4 * ((kr0 >> 1) & 1))) + 8 * (i16 & 1));
+  const uint32_t b_hi = uint32_t(kTAB + (kr0 + 4) * kTRowB + 16 * (q ^ (4 * (((kr0 + 4) >> 1) & 1))) + 8 * (i16 & 1));
+
+  f32x16 acc[2];  // even and odd k-steps: two independent accumulation chains
+#pragma unroll
+  for (int x = 0; x < 16; ++x) acc[0][x] = acc[1][x] = 0.f;
+
+#pragma unroll
+  for (int c = 0; c < kTStages - 1; ++c)
+    if (c < nchunks) issue(c);
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c landed (the four transfers of each later chunk issued may still fly), for every wave
+    // after the barrier; the stage of chunk c-1 is then free for chunk c+3
+    if (c + 2 < nchunks)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (c + 1 < nchunks)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (c + kTStages - 1 < nchunks) issue(c + kTStages - 1);
+    const uint32_t st = lds0 + uint32_t((c % kTStages) * kTStageB);
+    bf16x8 a[kKC / 16], b[kKC / 16];
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s) {
+      // the k-steps of A's 32 rows sit 32 bytes apart in the logical row: XOR of the chunk bit 1
+      a[s] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          reinterpret_cast<lds_u8*>(uintptr_t(st + (a_off ^ uint32_t(32 * s)))));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) i16x4*>(uintptr_t(st + b_lo + 16 * kTRowB * s)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) i16x4*>(uintptr_t(st + b_hi + 16 * kTRowB * s)));
+      b[s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s)
+      acc[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], b[s], acc[s & 1], 0, 0, 0);
+  }
+
+  // D layout: column l%32, rows 8*(x/4) + 4*(l/32) + x%4
+  float* const out = part + (size_t(ks) * rows) * kW + col0 + 32 * wn + (lane & 31);
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const int r = row0 + 32 * wm + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+    if (r < rows) out[size_t(r) * kW] = acc[0][x] + acc[1][x];
+  }
+}
+
 // RoPE inverse frequencies base^(-2i/d_r), computed on the host in double.
 struct InvFreq {
   double v[kDr / 2];
@@ -232,6 +365,8 @@ __global__ __launch_bounds__(64 * kFinishWaves) void kv_finish_kernel(const floa
 
 // K splits for `rows` new tokens: enough workgroups (about two per CU) to keep every CU
 // streaming weights, each split a whole number of 256-row chunks.
+constexpr int kTiledMinRows = 512;  // from here on kv_gemm_tiled_kernel (same splits, same partials)
+
 int kv_splits(int d_model, int rows) {
   const int nchunk = d_model / kChunk;
   const int tiles = kColTiles * ((rows + kRowsWg - 1) / kRowsWg);
@@ -283,10 +418,14 @@ hipError_t launch_kv_append_mfma(const Dims& d, const Cache& c, int d_model, con
                                  const void* w_kr, const int32_t* seq_ids, const int32_t* positions, int rows,
                                  float rms_eps, float* workspace, hipStream_t s, bool fp8) {
   const int splits = kv_splits(d_model, rows);
-  const dim3 grid(kColTiles, (rows + kRowsWg - 1) / kRowsWg, splits);
-  kv_gemm_kernel<<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(h), d_model, rows,
-                                           static_cast<const uint16_t*>(w_dkv), static_cast<const uint16_t*>(w_kr),
-                                           d_model / splits, workspace);
+  if (rows >= kTiledMinRows)
+    kv_gemm_tiled_kernel<<<kTColTiles * ((rows + kTM - 1) / kTM) * splits, kTThreads, 0, s>>>(
+        static_cast<const uint16_t*>(h), d_model, rows, static_cast<const uint16_t*>(w_dkv),
+        static_cast<const uint16_t*>(w_kr), d_model / splits, workspace);
+  else
+    kv_gemm_kernel<<<dim3(kColTiles, (rows + kRowsWg - 1) / kRowsWg, splits), kThreads, 0, s>>>(
+        static_cast<const uint16_t*>(h), d_model, rows, static_cast<const uint16_t*>(w_dkv),
+        static_cast<const uint16_t*>(w_kr), d_model / splits, workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   InvFreq inv;

@@ -82,12 +82,14 @@ def test_kv_append_v3(name):
     _check(t, w, pool, EPS, name)
 
 
-@pytest.mark.parametrize("rows,d_model", [(1, 256), (37, 768), (65, 4096), (130, 1024)])
+@pytest.mark.parametrize("rows,d_model", [(1, 256), (37, 768), (65, 4096), (130, 1024), (513, 256), (600, 768),
+                                          (1000, 4096)])
 def test_kv_append_edges(rows, d_model):
-    """Row counts off the 64-row tile, single-chunk and odd-chunk-count hidden widths."""
+    """Row counts off the 64-row tile, single-chunk and odd-chunk-count hidden widths; from 512 rows
+    on the tiled product (64 x 64 tiles, 64-k chunks), with ragged last tiles."""
     base = gen.WORKLOADS["v3_kv_append_b64"]
     w = gen.Workload(name="kv_edge", seed=11 + rows, kind="kv_append", batch=base.batch, ctx_range=base.ctx_range,
-                     q_len=3, random_pages=True, d_model=d_model)
+                     q_len=max(3, -(-rows // base.batch)), random_pages=True, d_model=d_model)
     t = gen.make_kv_append_inputs(w, rows=rows)
     note(f"kv_append edge rows={rows} d_model={d_model}")
     pool, _ = _run(t, w, EPS)
