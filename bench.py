@@ -394,9 +394,10 @@ def bench_prefill(args, w) -> dict:
 
 def bench_verify(args, w) -> dict:
     """Multi-token verify: q_len draft tokens per sequence of a ragged decode batch, each a decode
-    row over its own prefix.  Step: mla_verify_rows -> absorb -> balanced decode -> combine ->
-    out_proj.  The same inputs through mla_prefill_chunk (one workgroup per query row) are timed
-    beside it for comparison."""
+    row over its own prefix.  Step: mla_verify_rows -> absorb -> balanced decode with the draft
+    rows of a sequence as one row group (mla_decode_partial_grouped) -> combine -> out_proj.  The
+    same rows on the plain balanced split, and the same inputs through mla_prefill_chunk (one
+    workgroup per query row), are timed beside it for comparison."""
     import numpy as np
     import torch
 
@@ -434,8 +435,64 @@ def bench_verify(args, w) -> dict:
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
     ms_dec = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_dec_plain = ms_pf = None
+    if not args.no_compare:
+        ms_dec_plain, ms_pf = _verify_comparisons(args, inp, dev, n_units, stream)
+    achieved = read_bytes / (ms_dec * 1e-3) / 1e9
+    flops = int(row_lens.sum()) * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
+    return {
+        "metric": "MLA multi-token verify draft tokens/s (V3 shape, 1 GPU)",
+        "value": round(rows / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "draft_tokens": w.q_len, "heads": w.n_heads,
+                   "d_c": w.d_c, "d_r": w.d_r, "rows": rows,
+                   "split": f"balanced {st.n_units} units, row groups of {st.group}",
+                   "unique_cache_bytes": unique_bytes, "seed": w.seed},
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_partial_grouped (verify rows)",
+                     "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(w.name, _kernel_sha()),
+                     "ms_per_launch": round(ms_dec, 6), "algorithmic_bytes_per_launch": read_bytes,
+                     "unique_bytes_per_launch": unique_bytes,
+                     "unique_gbs": round(unique_bytes / (ms_dec * 1e-3) / 1e9, 3),
+                     "note": "every draft row reads its own prefix (algorithmic bytes); the rows of one "
+                             "sequence run side by side on one XCD, so repeats are served by its L2"},
+        "plain_balanced_ms_per_launch": None if ms_dec_plain is None else round(ms_dec_plain, 6),
+        "roofline_mfma": {"achieved": round(flops / (ms_dec * 1e-3) / 1e12, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(flops / (ms_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "prefill_chunk_ms_per_step": None if ms_pf is None else round(ms_pf, 6),
+    } | ({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_verify(inp, args.cpu_seconds)})
+
+
+def _verify_comparisons(args, inp, dev, n_units, stream):
+    """Decode-launch ms of the same verify rows on the plain balanced split (each draft row
+    scheduled on its own) and step ms of the same inputs through mla_prefill_chunk."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_31_amd import runner
+
+    sp = runner.VerifyStep(inp, dev, n_units=n_units, grouped=False)
+    n_sp = max(5, args.steps // 10)
+    for _ in range(3):
+        sp.run()
+    torch.cuda.synchronize()
+    ev_sp = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_sp)]
+    for a, b in ev_sp:
+        sp.rows()
+        sp.absorb()
+        a.record(stream)
+        sp.attend()
+        b.record(stream)
+        sp.combine()
+        sp.out_proj()
+    torch.cuda.synchronize()
+    ms_dec_plain = float(np.mean([a.elapsed_time(b) for a, b in ev_sp]))
+    del sp
     # the same verify through mla_prefill_chunk, for comparison
     pf = runner.PrefillStep(inp, dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_pf = max(5, args.steps // 10)
     for _ in range(3):
         pf.run()
@@ -446,26 +503,7 @@ def bench_verify(args, w) -> dict:
     stop.record(stream)
     torch.cuda.synchronize()
     ms_pf = start.elapsed_time(stop) / n_pf
-    achieved = read_bytes / (ms_dec * 1e-3) / 1e9
-    flops = int(row_lens.sum()) * w.n_heads * (2 * (w.d_c + w.d_r) + 2 * w.d_c)
-    return {
-        "metric": "MLA multi-token verify draft tokens/s (V3 shape, 1 GPU)",
-        "value": round(rows / (ms_step * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "draft_tokens": w.q_len, "heads": w.n_heads,
-                   "d_c": w.d_c, "d_r": w.d_r, "rows": rows, "split": f"balanced {n_units} units",
-                   "unique_cache_bytes": unique_bytes, "seed": w.seed},
-        "roofline": {"bound": "hbm", "kernel": "mla_decode_partial_balanced (verify rows)",
-                     "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "ms_per_launch": round(ms_dec, 6), "algorithmic_bytes_per_launch": read_bytes,
-                     "note": "rows of one sequence read the same prefix; repeats may hit L2/MALL"},
-        "roofline_mfma": {"achieved": round(flops / (ms_dec * 1e-3) / 1e12, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": round(flops / (ms_dec * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "prefill_chunk_ms_per_step": round(ms_pf, 6),
-    } | ({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_verify(inp, args.cpu_seconds)})
+    return ms_dec_plain, ms_pf
 
 
 def bench_precomposed(args, w) -> dict:
@@ -681,6 +719,8 @@ def main() -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/decode_traffic_<workload>.json from two rocprofv3 --pmc runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="verify workloads: skip the plain-split and prefill comparisons (counter runs)")
     ap.add_argument("--fp8", action="store_true",
                     help="decode workloads: FP8 latent cache (the bf16 pool quantised on the GPU first)")
     ap.add_argument("--unabsorbed", action="store_true",
@@ -708,6 +748,12 @@ def main() -> int:
     from mla_workloads import gen
 
     w = gen.WORKLOADS[args.workload]
+    if args.copy_probe_mb:  # a plain streaming copy of known size, for counter calibration
+        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device=torch.device("cuda:0"))
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if w.kind == "prefill":
         print(json.dumps(bench_prefill_unabsorbed(args, w) if args.unabsorbed else bench_prefill(args, w)), flush=True)
         return 0
@@ -725,12 +771,6 @@ def main() -> int:
         return 2
     inp = gen.make_decode_inputs(w)
     dev = torch.device("cuda:0")
-    if args.copy_probe_mb:  # a plain streaming copy of known size, for counter calibration
-        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
     flags = 0
     inp_dev = inp
     if args.fp8:  # FP8 rows of the same latents, quantised on the GPU (mla_quantize_rows_fp8)

@@ -211,6 +211,26 @@ mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* ca
 mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
                                 const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream);
 
+/* Balanced split with row groups, for the draft rows of a multi-token verify step ([molayo] key
+ * concept 5, speculative decoding; [ase] causal-mask remark after Fig. 2): batch rows in
+ * batch / row_group groups of row_group consecutive rows that read the same sequence's keys,
+ * each up to its own seq_lens entry (the rows mla_verify_rows writes).  The split above runs
+ * over groups, a group costing like its longest row, with n_units / row_group group-units;
+ * unit row_group*w + i runs row i of every group segment (w, g), clamped to that row's tokens,
+ * and writes its partial to slot row_group*(w + g) + i.  The row_group units of a group-unit
+ * read the same pages side by side (and share an L2), so the cache is fetched about once per
+ * group.  Results equal those of the plain balanced split up to the order of summation
+ * (different segment boundaries); row_group = 1 is mla_decode_partial_balanced.
+ *   row_group  >= 1, dividing both batch and n_units (MLA_ERR_SHAPE otherwise)
+ *   workspace, workspace_bytes  as for mla_decode_partial_balanced (the same size suffices)
+ * mla_combine_grouped merges what mla_decode_partial_grouped wrote with the same n_units and
+ * row_group, as mla_combine_balanced does for the plain split. */
+mla_status mla_decode_partial_grouped(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                      int32_t n_units, int32_t row_group, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+mla_status mla_combine_grouped(const mla_dims* dims, const mla_cache* cache, int32_t n_units, int32_t row_group,
+                               const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream);
+
 /* Value up-projection applied once after the weighted sum ([ase] "Value 투영을 가중합 뒤로
  * 옮기기", Fig. 4 equation; [huny] section 2, value absorption):
  *   out[r,h,:] = z[r,h,:] . W_UV[h]

@@ -74,6 +74,8 @@ _SIGNATURES = {
     "mla_decode_balanced_workspace_bytes": (ctypes.c_size_t, [_PD, _PC, _I32]),
     "mla_decode_partial_balanced": (_I32, [_PD, _PC, _VP, _I32, _VP, ctypes.c_size_t, _VP]),
     "mla_combine_balanced": (_I32, [_PD, _PC, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "mla_decode_partial_grouped": (_I32, [_PD, _PC, _VP, _I32, _I32, _VP, ctypes.c_size_t, _VP]),
+    "mla_combine_grouped": (_I32, [_PD, _PC, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
@@ -224,6 +226,20 @@ def mla_combine_balanced(d: MlaDims, c: MlaCache, n_units: int, workspace, works
     _check(library().mla_combine_balanced(ctypes.byref(d), ctypes.byref(c), n_units, _addr(workspace),
                                           workspace_bytes, _addr(z), _addr(lse), _stream(stream)),
            "mla_combine_balanced")
+
+
+def mla_decode_partial_grouped(d: MlaDims, c: MlaCache, q_hat, n_units: int, row_group: int, workspace,
+                               workspace_bytes: int, stream=None) -> None:
+    _check(library().mla_decode_partial_grouped(ctypes.byref(d), ctypes.byref(c), _addr(q_hat), n_units, row_group,
+                                                _addr(workspace), workspace_bytes, _stream(stream)),
+           "mla_decode_partial_grouped")
+
+
+def mla_combine_grouped(d: MlaDims, c: MlaCache, n_units: int, row_group: int, workspace, workspace_bytes: int, z,
+                        lse=None, stream=None) -> None:
+    _check(library().mla_combine_grouped(ctypes.byref(d), ctypes.byref(c), n_units, row_group, _addr(workspace),
+                                         workspace_bytes, _addr(z), _addr(lse), _stream(stream)),
+           "mla_combine_grouped")
 
 
 def mla_out_proj(d: MlaDims, z, w_uv, rows: int, out, stream=None) -> None:

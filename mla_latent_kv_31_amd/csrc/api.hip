@@ -60,6 +60,12 @@ mla_status check_balanced(const Cache& c, int n_units) {
   return MLA_OK;
 }
 
+// Row groups of the balanced split: G consecutive rows per group, G dividing batch and n_units.
+mla_status check_group(const Cache& c, int n_units, int group) {
+  if (group < 1 || c.batch % group != 0 || n_units % group != 0) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
 mla_status ptr_ok(const void* p) {
   if (!p) return MLA_ERR_NULL;
   return aligned16(p) ? MLA_OK : MLA_ERR_ALIGN;
@@ -231,40 +237,55 @@ size_t mla_decode_balanced_workspace_bytes(const mla_dims* dims, const mla_cache
   return slots < 0 ? 0 : partials_bytes(d, slots);
 }
 
-mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
-                                       int32_t n_units, void* workspace, size_t workspace_bytes, void* stream) {
+mla_status mla_decode_partial_grouped(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                      int32_t n_units, int32_t row_group, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   Dims d;
   Cache c;
   Partials p;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   MLA_TRY(check_balanced(c, n_units));
+  MLA_TRY(check_group(c, n_units, row_group));
   MLA_TRY(ptr_ok(q_hat));
   MLA_TRY(check_workspace(d, mla_balanced_num_slots(c.batch, n_units), workspace, workspace_bytes, &p));
   const bool mfma = !generic_forced(dims) && decode_mfma_supported(d, c, 0);
   if (cache_fp8(dims) && !mfma) return MLA_ERR_UNSUPPORTED;
   if (c.batch == 0) return MLA_OK;
   if (mfma)
-    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, p.o, p.lse, (hipStream_t)stream,
+    return hip_status(launch_decode_mfma_balanced(d, c, q_hat, n_units, row_group, p.o, p.lse, (hipStream_t)stream,
                                                   cache_fp8(dims)));
-  return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, p.o, p.lse, (hipStream_t)stream));
+  return hip_status(launch_decode_generic_balanced(d, c, q_hat, n_units, row_group, p.o, p.lse, (hipStream_t)stream));
 }
 
-mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
-                                const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream) {
+mla_status mla_decode_partial_balanced(const mla_dims* dims, const mla_cache* cache, const void* q_hat,
+                                       int32_t n_units, void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_partial_grouped(dims, cache, q_hat, n_units, 1, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_combine_grouped(const mla_dims* dims, const mla_cache* cache, int32_t n_units, int32_t row_group,
+                               const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream) {
   Dims d;
   Cache c;
   Partials p;
   MLA_TRY(check_dims(dims, &d));
   MLA_TRY(check_cache(cache, &c));
   MLA_TRY(check_balanced(c, n_units));
+  MLA_TRY(check_group(c, n_units, row_group));
   MLA_TRY(check_workspace(d, mla_balanced_num_slots(c.batch, n_units), workspace, workspace_bytes, &p));
   MLA_TRY(ptr_ok(z));
   if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
   if (c.batch == 0) return MLA_OK;
   if (!(dims->flags & MLA_FLAG_FORCE_GENERIC) && combine_fast_supported(d, n_units))
-    return hip_status(launch_combine_fast_balanced(d, c, n_units, p.o, p.lse, z, lse, (hipStream_t)stream));
-  return hip_status(launch_combine_generic_balanced(d, c, n_units, p.o, p.lse, z, lse, (hipStream_t)stream));
+    return hip_status(
+        launch_combine_fast_balanced(d, c, n_units, row_group, p.o, p.lse, z, lse, (hipStream_t)stream));
+  return hip_status(
+      launch_combine_generic_balanced(d, c, n_units, row_group, p.o, p.lse, z, lse, (hipStream_t)stream));
+}
+
+mla_status mla_combine_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                const void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream) {
+  return mla_combine_grouped(dims, cache, n_units, 1, workspace, workspace_bytes, z, lse, stream);
 }
 
 mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,

@@ -18,10 +18,12 @@ namespace {
 constexpr int kCombineMaxSplits = 2048;
 
 // grid (H / 4, batch); wave w handles head 4*blockIdx.x + w.  The partials of sequence b are the
-// `count` consecutive slots from `base`: the S chunks b*S .. b*S+S-1 of the fixed split, or the
-// slots of b's segments in the balanced split (recomputed from seq_lens, see schedule.h).
+// `count` slots base, base + step, ...: the S chunks b*S .. b*S+S-1 of the fixed split, or the
+// slots of b's segments in the balanced split with row groups of `group` rows (recomputed from
+// seq_lens, see schedule.h; consecutive for group 1, every group-th slot otherwise).
 template <bool kBalanced>
-__global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, int group,
+                                                      const int32_t* __restrict__ seq_lens,
                                                       int batch, int cap, const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, float* __restrict__ z,
                                                       float* __restrict__ lse_out) {
@@ -29,22 +31,25 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = 4 * blockIdx.x + wave, b = blockIdx.y;
   if (h >= H) return;  // whole wave leaves; no block-wide barrier follows
-  int base = b * S, count = S;
+  int base = b * S, count = S, step = 1;
   if constexpr (kBalanced) {
+    const int grp = b / group, gi = b - grp * group;
     int cb, total;
-    sched_prefix(seq_lens, batch, cap, b, cb, total);
-    const int tiles = sched_tiles(sched_len(seq_lens[b], cap));
+    sched_prefix(seq_lens, batch / group, group, cap, grp, cb, total);
+    const int tiles = sched_tiles(sched_len(seq_lens[b], cap));  // this row's own tiles
     count = 0;
     if (tiles > 0) {
       int w0, w1;
-      sched_units(cb, tiles, sched_quota(total, S), w0, w1);
-      base = w0 + b;
+      sched_units(cb, tiles, sched_quota(total, S / group), w0, w1);
+      base = sched_slot(w0, grp, group, gi);
       count = w1 - w0 + 1;
+      step = group;
     }
   }
   const float* lp = lse_part + size_t(base) * H + h;
+  const size_t lstride = size_t(step) * H;
   float mx = -INFINITY;
-  for (int s = lane; s < count; s += 64) mx = fmaxf(mx, lp[size_t(s) * H]);
+  for (int s = lane; s < count; s += 64) mx = fmaxf(mx, lp[s * lstride]);
   mx = wave_max(mx);
   float* zo = z + (size_t(b) * H + h) * dc;
   if (mx == -INFINITY) {
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
   }
   float tot = 0.f;
   for (int s = lane; s < count; s += 64) {
-    const float w = expf(lp[size_t(s) * H] - mx);
+    const float w = expf(lp[s * lstride] - mx);
     wts[wave][s] = w;
     tot += w;
   }
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int dc, int S, cons
   const int c0 = 8 * lane;
   if (c0 < dc) {
     const float* op = o_part + (size_t(base) * H + h) * dc + c0;
-    const size_t stride = size_t(H) * dc;
+    const size_t stride = size_t(step) * H * dc;
     // eight slots per round: all sixteen loads are issued before the first FMA.  Rows of zero
     // weight (empty chunks, possibly never written) are loaded but dropped by a select.
     constexpr int kG = 8;
@@ -108,15 +113,15 @@ bool combine_fast_supported(const Dims& d, int n_splits) {
 
 hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                float* z, float* lse, hipStream_t s) {
-  combine_kernel<false><<<dim3((d.H + 3) / 4, batch), 256, 0, s>>>(d.H, d.dc, n_splits, nullptr, batch, 0, o_part,
+  combine_kernel<false><<<dim3((d.H + 3) / 4, batch), 256, 0, s>>>(d.H, d.dc, n_splits, 1, nullptr, batch, 0, o_part,
                                                                    lse_part, z, lse);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, int group, const float* o_part,
                                         const float* lse_part, float* z, float* lse, hipStream_t s) {
   combine_kernel<true><<<dim3((d.H + 3) / 4, c.batch), 256, 0, s>>>(
-      d.H, d.dc, n_units, c.seq_lens, c.batch, c.max_pages * c.page_size, o_part, lse_part, z, lse);
+      d.H, d.dc, n_units, group, c.seq_lens, c.batch, c.max_pages * c.page_size, o_part, lse_part, z, lse);
   return hipGetLastError();
 }
 

@@ -290,20 +290,26 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
 
   // ---- the segment list.  Workgroups are dealt to the chip's eight XCDs (each with its own L2) in
   // turn, workgroup id modulo 8; consecutive units of the work-balanced split, which mostly share
-  // a sequence (and so its q_hat rows and page-table row), are placed on one XCD.
+  // a sequence (and so its q_hat rows and page-table row), or are the rows of one row group
+  // reading the same pages side by side, are placed on one XCD.
   int unit = blockIdx.x;
   if constexpr (kBal) {
     if (gridDim.x % kXcds == 0) unit = (unit % kXcds) * (gridDim.x / kXcds) + unit / kXcds;
   }
+  // kBalanced: split_tokens carries the row-group size G (schedule.h); this unit runs row g_row of
+  // the groups in group-unit g_unit
+  const int group = kBal ? split_tokens : 1;
+  const int g_unit = unit / group, g_row = unit - g_unit * group;
+  const int n_groups = batch / group;
   int next_b, next_cb = 0, unit_end = 0, quota = 0;
   if constexpr (kBal) {
     int total;
-    sched_prefix(seq_lens, batch, cap, 0, next_cb, total);
+    sched_prefix(seq_lens, n_groups, group, cap, 0, next_cb, total);
     total = __builtin_amdgcn_readfirstlane(total);  // wave-uniform: keep the segment loop scalar
-    quota = sched_quota(total, n_splits);
-    if (quota == 0 || unit * quota >= total) return;  // idle unit (uniform)
-    unit_end = min(unit * quota + quota, total);
-    sched_find(seq_lens, batch, cap, unit * quota, next_b, next_cb);
+    quota = sched_quota(total, n_splits / group);
+    if (quota == 0 || g_unit * quota >= total) return;  // idle unit (uniform)
+    unit_end = min(g_unit * quota + quota, total);
+    sched_find(seq_lens, n_groups, group, cap, g_unit * quota, next_b, next_cb);
     next_b = __builtin_amdgcn_readfirstlane(next_b);
     next_cb = __builtin_amdgcn_readfirstlane(next_cb);
   } else {
@@ -314,17 +320,19 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     int b, t0, t1;
     size_t slot, qrow;  // output row group and q_hat row group (128 heads each)
     if constexpr (kBal) {
-      if (next_b >= batch || next_cb >= unit_end) break;
-      b = next_b;
-      const int len = sched_len(seq_lens[b], cap);
+      if (next_b >= n_groups || next_cb >= unit_end) break;
+      const int grp = next_b;
+      b = grp * group + g_row;
+      const int glen = group == 1 ? sched_len(seq_lens[b], cap) : sched_group_len(seq_lens, grp, group, cap);
+      const int len = group == 1 ? glen : sched_len(seq_lens[b], cap);
       int k0, k1;
-      sched_segment(next_cb, sched_tiles(len), unit, quota, k0, k1);
-      next_cb += sched_cost(len);
+      sched_row_segment(next_cb, sched_tiles(glen), sched_tiles(len), g_unit, quota, k0, k1);
+      next_cb += sched_cost(glen);
       ++next_b;
-      if (k1 <= k0) continue;  // this unit holds only the segment price of sequence b
+      if (k1 <= k0) continue;  // only the segment price of this group, or past this row's end
       t0 = k0 * kTile;
       t1 = min(k1 * kTile, len);
-      slot = size_t(unit) + b;
+      slot = size_t(sched_slot(g_unit, grp, group, g_row));
       qrow = b;
     } else if constexpr (MODE == kPrefill) {
       // n_splits carries the chunk length; row i of sequence b reads keys t <= q_start[b] + i
@@ -832,14 +840,14 @@ hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
-                                       float* lse_part, hipStream_t s, bool fp8) {
+hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, int group,
+                                       float* o_part, float* lse_part, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
   auto k = fp8 ? decode_mfma_kernel<kBalanced, true> : decode_mfma_kernel<kBalanced, false>;
   k<<<dim3(n_units), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
-      static_cast<const uint16_t*>(q_hat), n_units, 0, nullptr, o_part, lse_part);
+      static_cast<const uint16_t*>(q_hat), n_units, group, nullptr, o_part, lse_part);
   return hipGetLastError();
 }
 

@@ -76,15 +76,20 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache 
     qrow = (size_t(b) * q_len + x) * d.H + h;
     orow = qrow;
   } else if (MODE == kBalanced) {
+    // split_tokens carries the row-group size G: unit x runs row x % G of its group-unit x / G
+    const int group = split_tokens, cap = c.max_pages * c.page_size;
+    const int gu = x / group, gi = x - gu * group, grp = b / group;
+    if (b - grp * group != gi) return;  // another unit's row (uniform over the block)
     int cb, total;
-    sched_prefix(c.seq_lens, c.batch, c.max_pages * c.page_size, b, cb, total);
+    sched_prefix(c.seq_lens, c.batch / group, group, cap, grp, cb, total);
     int k0, k1;
-    sched_segment(cb, sched_tiles(len), x, sched_quota(total, n_splits), k0, k1);
+    sched_row_segment(cb, sched_tiles(sched_group_len(c.seq_lens, grp, group, cap)), sched_tiles(len), gu,
+                      sched_quota(total, n_splits / group), k0, k1);
     if (k1 <= k0) return;  // uniform over the block
     t0 = k0 * kSchedTile;
     t1 = min(k1 * kSchedTile, len);
     qrow = size_t(b) * d.H + h;
-    orow = (size_t(x) + b) * d.H + h;
+    orow = size_t(sched_slot(gu, grp, group, gi)) * d.H + h;
   } else {
     t0 = x * split_tokens;
     t1 = min(t0 + split_tokens, len);
@@ -141,7 +146,8 @@ __global__ __launch_bounds__(kThreads) void attend_generic_kernel(Dims d, Cache 
 // One block per (head, sequence): LSE-weighted merge of the sequence's partials, the S chunks of
 // the fixed split or the segment slots of the balanced split (schedule.h).
 template <bool BAL>
-__global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache c, int S, const float* __restrict__ o_part,
+__global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache c, int S, int group,
+                                                                   const float* __restrict__ o_part,
                                                                    const float* __restrict__ lse_part,
                                                                    float* __restrict__ z,
                                                                    float* __restrict__ lse_out) {
@@ -149,23 +155,26 @@ __global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache
   __shared__ float wts[1024];
   const int h = blockIdx.x, b = blockIdx.y;
   size_t base = size_t(b) * S;
-  int count = S;
+  int count = S, step = 1;
   if (BAL) {
     const int cap = c.max_pages * c.page_size;
+    const int grp = b / group, gi = b - grp * group;
     int cb, total;
-    sched_prefix(c.seq_lens, c.batch, cap, b, cb, total);
-    const int tiles = sched_tiles(sched_len(c.seq_lens[b], cap));
+    sched_prefix(c.seq_lens, c.batch / group, group, cap, grp, cb, total);
+    const int tiles = sched_tiles(sched_len(c.seq_lens[b], cap));  // this row's own tiles
     count = 0;
     if (tiles > 0) {
       int w0, w1;
-      sched_units(cb, tiles, sched_quota(total, S), w0, w1);
-      base = size_t(w0) + b;
+      sched_units(cb, tiles, sched_quota(total, S / group), w0, w1);
+      base = size_t(sched_slot(w0, grp, group, gi));
       count = w1 - w0 + 1;
+      step = group;
     }
   }
-  const float* lp = lse_part + base * d.H + h;  // stride H over partials
+  const float* lp = lse_part + base * d.H + h;  // stride step * H over partials
+  const size_t lstride = size_t(step) * d.H;
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < count; s += blockDim.x) mx = fmaxf(mx, lp[size_t(s) * d.H]);
+  for (int s = threadIdx.x; s < count; s += blockDim.x) mx = fmaxf(mx, lp[s * lstride]);
   mx = block_max(mx, red);
   float* zo = z + (size_t(b) * d.H + h) * d.dc;
   if (mx == -INFINITY) {
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache
     return;
   }
   float tot = 0.f;
-  for (int s = threadIdx.x; s < count; s += blockDim.x) tot += expf(lp[size_t(s) * d.H] - mx);
+  for (int s = threadIdx.x; s < count; s += blockDim.x) tot += expf(lp[s * lstride] - mx);
   tot = block_sum(tot, red);
   const float inv = 1.f / tot;
   float acc[kGenericMaxDc / kThreads];
@@ -183,12 +192,12 @@ __global__ __launch_bounds__(kThreads) void combine_generic_kernel(Dims d, Cache
   for (int s0 = 0; s0 < count; s0 += 1024) {
     const int ns = min(1024, count - s0);
     __syncthreads();
-    for (int s = threadIdx.x; s < ns; s += blockDim.x) wts[s] = expf(lp[size_t(s0 + s) * d.H] - mx) * inv;
+    for (int s = threadIdx.x; s < ns; s += blockDim.x) wts[s] = expf(lp[(s0 + s) * lstride] - mx) * inv;
     __syncthreads();
     for (int s = 0; s < ns; ++s) {
       const float w = wts[s];
       if (w == 0.f) continue;  // empty chunk: its partial is never read
-      const float* op = o_part + ((base + s0 + s) * d.H + h) * d.dc;
+      const float* op = o_part + ((base + size_t(s0 + s) * step) * d.H + h) * d.dc;
 #pragma unroll
       for (int i = 0; i < kGenericMaxDc / kThreads; ++i) {
         const int j = threadIdx.x + i * kThreads;
@@ -340,26 +349,28 @@ hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_h
 hipError_t launch_combine_generic(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                   float* z, float* lse, hipStream_t s) {
   Cache none{};
-  combine_generic_kernel<false><<<dim3(d.H, batch), kThreads, 0, s>>>(d, none, n_splits, o_part, lse_part, z, lse);
+  combine_generic_kernel<false><<<dim3(d.H, batch), kThreads, 0, s>>>(d, none, n_splits, 1, o_part, lse_part, z, lse);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units,
+hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, int group,
                                           float* o_part, float* lse_part, hipStream_t s) {
   const dim3 grid(n_units, c.batch, d.H);
   const size_t shm = sizeof(float) * (d.W() + kThreads + 16);
   if (d.dtype == MLA_BF16)
-    attend_generic_kernel<uint16_t, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const f16_t*)q_hat, 0, n_units, 1,
-                                                                          nullptr, o_part, lse_part);
+    attend_generic_kernel<uint16_t, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const f16_t*)q_hat, group, n_units,
+                                                                          1, nullptr, o_part, lse_part);
   else
-    attend_generic_kernel<float, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, 0, n_units, 1,
-                                                                       nullptr, o_part, lse_part);
+    attend_generic_kernel<float, kBalanced><<<grid, kThreads, shm, s>>>(d, c, (const float*)q_hat, group, n_units,
+                                                                       1, nullptr, o_part, lse_part);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
-                                           const float* lse_part, float* z, float* lse, hipStream_t s) {
-  combine_generic_kernel<true><<<dim3(d.H, c.batch), kThreads, 0, s>>>(d, c, n_units, o_part, lse_part, z, lse);
+hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, int group,
+                                           const float* o_part, const float* lse_part, float* z, float* lse,
+                                           hipStream_t s) {
+  combine_generic_kernel<true><<<dim3(d.H, c.batch), kThreads, 0, s>>>(d, c, n_units, group, o_part, lse_part, z,
+                                                                       lse);
   return hipGetLastError();
 }
 

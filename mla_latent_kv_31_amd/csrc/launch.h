@@ -33,8 +33,9 @@ constexpr int kGenericMaxDk = 1024;
 bool decode_mfma_supported(const Dims& d, const Cache& c, int split_tokens);
 hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, int n_splits, int split_tokens,
                               float* o_part, float* lse_part, hipStream_t s, bool fp8 = false);
-hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, float* o_part,
-                                       float* lse_part, hipStream_t s, bool fp8 = false);
+// balanced split over n_units units with row groups of `group` rows (schedule.h; 1: plain split)
+hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, int group,
+                                       float* o_part, float* lse_part, hipStream_t s, bool fp8 = false);
 // chunked prefill on the same kernel: one workgroup per query row over its causal key range
 bool prefill_mfma_supported(const Dims& d, const Cache& c);
 hipError_t launch_prefill_mfma(const Dims& d, const Cache& c, const void* q_hat, int q_len, const int32_t* q_start,
@@ -49,7 +50,7 @@ hipError_t launch_out_proj_mfma(const Dims& d, const float* z, const void* w_uv,
 bool combine_fast_supported(const Dims& d, int n_splits);
 hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const float* o_part, const float* lse_part,
                                float* z, float* lse, hipStream_t s);
-hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
+hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, int group, const float* o_part,
                                         const float* lse_part, float* z, float* lse, hipStream_t s);
 
 hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
@@ -60,10 +61,11 @@ hipError_t launch_prefill_generic(const Dims& d, const Cache& c, const void* q_h
                                   const int32_t* q_start, float* z, float* lse, hipStream_t s);
 hipError_t launch_combine_generic(const Dims& d, int batch, int n_splits, const float* o_part,
                                   const float* lse_part, float* z, float* lse, hipStream_t s);
-hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units,
+hipError_t launch_decode_generic_balanced(const Dims& d, const Cache& c, const void* q_hat, int n_units, int group,
                                           float* o_part, float* lse_part, hipStream_t s);
-hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, const float* o_part,
-                                           const float* lse_part, float* z, float* lse, hipStream_t s);
+hipError_t launch_combine_generic_balanced(const Dims& d, const Cache& c, int n_units, int group,
+                                           const float* o_part, const float* lse_part, float* z, float* lse,
+                                           hipStream_t s);
 hipError_t launch_out_proj_generic(const Dims& d, const float* z, const void* w_uv, int rows, float* out,
                                    hipStream_t s);
 hipError_t launch_project_query(const Dims& d, int d_model, int d_cq, const void* h, const void* w_dq,

@@ -199,10 +199,13 @@ class PrefillStep:
 class VerifyStep:
     """Device buffers of one multi-token verify call on the decode path: query i of sequence b
     becomes decode row b * q_len + i over its own prefix (mla_verify_rows writes the rows' page
-    table, lengths and positions), then the work-balanced decode over ``n_units`` workgroups.
+    table, lengths and positions), then the work-balanced decode over ``n_units`` workgroups with
+    the q_len rows of a sequence as one row group (mla_decode_partial_grouped: the draft rows of a
+    sequence read its pages side by side), or the plain balanced split when ``grouped`` is false.
+    ``n_units`` is rounded down to a multiple of q_len for the grouped split.
     Same inputs and outputs as PrefillStep (``out`` [B, q_len, H, d_v], ``lse`` [B, q_len, H])."""
 
-    def __init__(self, inp: dict, device="cuda:0", n_units: int = 256, flags: int = 0):
+    def __init__(self, inp: dict, device="cuda:0", n_units: int = 256, flags: int = 0, grouped: bool = True):
         w = inp["workload"]
         self.w = w
         self.device = torch.device(device)
@@ -219,7 +222,8 @@ class VerifyStep:
         self.B, self.Sq = int(inp["q_c"].shape[0]), int(inp["q_c"].shape[1])
         R = self.B * self.Sq
         H, W = w.n_heads, w.d_c + w.d_r
-        self.n_units = int(n_units)
+        self.group = self.Sq if grouped and int(n_units) >= self.Sq else 1
+        self.n_units = int(n_units) // self.group * self.group
         max_pages = int(self.page_table.shape[1])
         self.row_table = torch.empty((R, max_pages), dtype=torch.int32, device=dev)
         self.row_lens = torch.empty((R,), dtype=torch.int32, device=dev)
@@ -242,10 +246,12 @@ class VerifyStep:
         L.mla_absorb_query(self.d, self.q_c, self.q_r, self.w_uk, self.row_pos, self.B * self.Sq, self.q_hat, stream)
 
     def attend(self, stream=None):
-        L.mla_decode_partial_balanced(self.d, self.rc, self.q_hat, self.n_units, self.ws, self.ws_bytes, stream)
+        L.mla_decode_partial_grouped(self.d, self.rc, self.q_hat, self.n_units, self.group, self.ws, self.ws_bytes,
+                                     stream)
 
     def combine(self, stream=None):
-        L.mla_combine_balanced(self.d, self.rc, self.n_units, self.ws, self.ws_bytes, self.z, self.lse, stream)
+        L.mla_combine_grouped(self.d, self.rc, self.n_units, self.group, self.ws, self.ws_bytes, self.z, self.lse,
+                              stream)
 
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B * self.Sq, self.out, stream)

@@ -169,6 +169,30 @@ def test_balanced_validation():
     assert comb(_cache(batch=0)) == M.MLA_OK
 
 
+def test_grouped_validation():
+    """Row groups must be >= 1 and divide both the batch and the unit count; the workspace is the
+    plain balanced split's."""
+    lib = M.library()
+    d = _dims()
+
+    def dec(c, n=256, g=4, nbytes=BIG):
+        return lib.mla_decode_partial_grouped(ctypes.byref(d), ctypes.byref(c), A, n, g, B_, nbytes, None)
+
+    def comb(c, n=256, g=4, nbytes=BIG):
+        return lib.mla_combine_grouped(ctypes.byref(d), ctypes.byref(c), n, g, A, nbytes, A, None, None)
+
+    for fn in (dec, comb):
+        assert fn(_cache(), g=0) == M.MLA_ERR_SHAPE
+        assert fn(_cache(), g=-4) == M.MLA_ERR_SHAPE
+        assert fn(_cache(batch=6), g=4) == M.MLA_ERR_SHAPE      # 4 does not divide the batch
+        assert fn(_cache(batch=8), n=254, g=4) == M.MLA_ERR_SHAPE  # nor the units
+        assert fn(_cache(), n=0) == M.MLA_ERR_SHAPE
+        assert fn(_cache(batch=0)) == M.MLA_OK
+    need = M.mla_decode_balanced_workspace_bytes(d, _cache(), 256)
+    assert dec(_cache(), nbytes=need - 1) == M.MLA_ERR_WORKSPACE
+    assert comb(_cache(), nbytes=need - 1) == M.MLA_ERR_WORKSPACE
+
+
 def test_kv_append_workspace_validation():
     """The MFMA cache write needs a caller workspace of the advertised size; other shapes need none."""
     lib = M.library()

@@ -234,6 +234,66 @@ def test_spike_balanced(n_units, flags):
         assert np.allclose(lse[b], 128.0 * np.log(2.0), atol=1e-4), (L, t, lse[b, :2])
 
 
+# ------------------------------------------------------------------------------ row groups
+def _run_grouped(inp, n_units, group, q_hat_np, flags=0):
+    """The balanced split with row groups (mla_decode_partial_grouped / mla_combine_grouped) on
+    a DecodeStep's buffers; the plain split's workspace size suffices."""
+    st = runner.DecodeStep(inp, 0, DEV, flags=flags, n_units=n_units)
+    st.q_hat.copy_(runner.to_device(q_hat_np, DEV))
+    M.mla_decode_partial_grouped(st.d, st.c, st.q_hat, n_units, group, st.ws, st.ws_bytes)
+    M.mla_combine_grouped(st.d, st.c, n_units, group, st.ws, st.ws_bytes, st.z, st.lse)
+    torch.cuda.synchronize()
+    return st
+
+
+# verify-style groups (lengths base+1 .. base+G) and unrelated lengths, empty rows included
+GROUP_LENS = {2: [0, 1, 63, 64, 64, 65, 1000, 1025, 0, 0, 3000, 31, 500, 501, 32, 1],
+              4: [62, 63, 64, 65, 0, 1, 2, 3, 1022, 1023, 1024, 1025, 0, 0, 0, 0, 3000, 31, 33, 129]}
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("group,n_units", [(2, 2), (2, 16), (4, 4), (4, 16), (4, 256)])
+def test_count_grouped(group, n_units, flags):
+    """Zero query: every segment slot of the grouped split holds its exact token count, and each
+    row's merged lse its length."""
+    lens = GROUP_LENS[group]
+    note(f"count grouped group={group} n_units={n_units} flags={flags}")
+    inp = gen.make_decode_inputs(_w(len(lens)), lens=np.array(lens, np.int32), fill="nan")
+    st = _run_grouped(inp, n_units, group, np.zeros((len(lens), 128, 576), np.uint16), flags=flags)
+    lse_p = _np(st.lse_part)
+    segs = segments(lens, n_units, group=group)
+    assert segs and len({s[4] for s in segs}) == len(segs)
+    for u, r, t0, t1, slot in segs:
+        e = np.exp(lse_p[slot].astype(np.float64))
+        assert np.all(np.rint(e) == t1 - t0), (u, r, t0, t1, e[:4])
+    lse = _np(st.lse).astype(np.float64)
+    for r, L in enumerate(lens):
+        if L == 0:
+            assert np.all(lse[r] == -np.inf) and np.all(_np(st.z)[r] == 0)
+        else:
+            assert np.all(np.rint(np.exp(lse[r])) == L), r
+
+
+@pytest.mark.parametrize("flags", PATHS)
+@pytest.mark.parametrize("n_units", [4, 8, 256])
+def test_spike_grouped(n_units, flags):
+    """A 2^128-weight token at segment and length boundaries of rows in groups of 4."""
+    cases = []
+    for L in (1, 65, 1000, 1025):
+        cases += [(L, t) for t in sorted({0, 31, 32, L // 2, L - 1}) if t < L]
+    while len(cases) % 4:
+        cases.append((33, 32))
+    note(f"spike grouped n_units={n_units} flags={flags} cases={len(cases)}")
+    inp, q, rows = _spike_inputs(cases)
+    st = _run_grouped(inp, n_units, 4, q, flags=flags)
+    z, lse = _np(st.z), _np(st.lse)
+    for b, (L, t) in enumerate(cases):
+        want = gen.bf16_from_bits(rows[b][t, :512]).astype(np.float64)
+        err = np.max(np.abs(z[b] - want[None]))
+        assert err <= 1e-5, f"len {L} spike {t}: z off by {err}"
+        assert np.allclose(lse[b], 128.0 * np.log(2.0), atol=1e-4), (L, t, lse[b, :2])
+
+
 def test_long_segment_page_windows():
     """Segments longer than 64 pages move the page-id window inside the tile loop; with a spike
     near the end the rerun pass restarts from the first window.  Page size 32 (one tile per

@@ -51,18 +51,21 @@ def _check_against_prefill(inp, st):
     assert np.all(np.abs(la[fin] - lb[fin]) <= 2 * TOL["bf16"])
 
 
-def test_verify_small_ragged():
+@pytest.mark.parametrize("grouped", [True, False])
+def test_verify_small_ragged(grouped):
     """Five sequences with prior lengths 1..300 and four draft tokens; one verify window starts
     at -2 (its first two rows see no key: o = 0, lse = -inf), one at 0.  Every head of every row
-    against the oracle, every output against mla_prefill_chunk."""
+    against the oracle, every output against mla_prefill_chunk; with the draft rows of a sequence
+    as one row group (mla_decode_partial_grouped) and with the plain balanced split."""
     w = gen.Workload(name="verify_small", seed=21, kind="prefill", batch=5, ctx_range=(1, 300), q_len=4,
                      random_pages=True)
     inp = gen.make_prefill_inputs(w)
     inp["q_start"] = inp["q_start"].copy()
     inp["q_start"][1] = -2
     inp["q_start"][3] = 0
-    note(f"verify small ragged lens={inp['lens'].tolist()} q_start={inp['q_start'].tolist()}")
-    st = runner.VerifyStep(inp, DEV, n_units=16)
+    note(f"verify small ragged grouped={grouped} lens={inp['lens'].tolist()} q_start={inp['q_start'].tolist()}")
+    st = runner.VerifyStep(inp, DEV, n_units=16, grouped=grouped)
+    assert st.group == (4 if grouped else 1)
     st.run()
     torch.cuda.synchronize()
     _check_rows(inp, st)
@@ -86,6 +89,7 @@ def test_verify_v3_b64_sq4():
     inp = gen.make_prefill_inputs(gen.WORKLOADS["v3_verify_b64_sq4"])
     note("verify v3_verify_b64_sq4")
     st = runner.VerifyStep(inp, DEV, n_units=256)
+    assert st.group == 4
     st.run()
     torch.cuda.synchronize()
     _check_rows(inp, st)
