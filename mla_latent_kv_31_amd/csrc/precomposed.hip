@@ -75,15 +75,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
       for (int x = 0; x < 2; ++x) sa[x] = *reinterpret_cast<const u32x4*>(a + 8 * x);
     }
   };
-  // LDS layout of a buffer: B [64 k][128 n] bf16 (256-byte rows); A hi and A lo [64 m][64 k] bf16
-  // (128-byte rows, 16-byte chunk c of row r at c ^ (r & 7) against bank conflicts of the row reads)
-  auto a_chunk_off = [](int r, int c) { return r * 128 + 16 * (c ^ (r & 7)); };
+  // LDS layout of a buffer: B [64 k][128 n] bf16 (256-byte rows, 16-byte chunk c of k row k at
+  // c ^ 4(k & 3), so that the 4 k rows x 64 bytes of a transposing read fall in distinct bank
+  // groups); A hi and A lo [64 m][64 k] bf16 (128-byte rows, chunk c of row r at c ^ ((r >> 1) & 7):
+  // 16 consecutive rows at one logical chunk, two rows per 256-byte bank line, hit 16 bank groups)
+  auto a_chunk_off = [](int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); };
   auto store = [&](int buf) {
     lds_u8* const bb = lbase + buf * kBufB;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int p = t + kThreads * x;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + 16 * p) = sb[x];
+      const int p = t + kThreads * x, k = p >> 4;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + 256 * k + 16 * ((p & 15) ^ (4 * (k & 3)))) =
+          sb[x];
     }
     const int r = t >> 2;
     if constexpr (AF32) {
@@ -116,7 +119,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
   // B: transposing reads, group g = l/16 addresses k rows 8(g/2) + (l%16)/4 (+4) of step s and
   // columns 32w + 16(g%2) + 4(l%4) .. +3 (the kv-append GEMM's B layout with 256-byte rows).
   const int g = lane >> 4, i16 = lane & 15;
-  const int b_off = (8 * (g >> 1) + (i16 >> 2)) * (kTN * 2) + 2 * (32 * wave + 16 * (g & 1) + 4 * (i16 & 3));
+  // k row 8(g/2) + i16/4 (k & 3 = i16/4 for every step and the +4 read), 16-byte chunk
+  // 4w + 2(g%2) + (i16%4)/2, 8-byte half i16%2
+  const int b_off = (8 * (g >> 1) + (i16 >> 2)) * (kTN * 2) +
+                    16 * ((4 * wave + 2 * (g & 1) + ((i16 & 3) >> 1)) ^ (4 * (i16 >> 2))) + 8 * (i16 & 1);
   auto a_op = [&](const lds_u8* ab, int rb, int s) {
     const int r = 32 * rb + (lane & 31);
     return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(ab + a_chunk_off(r, 2 * s + (lane >> 5)));
