@@ -61,7 +61,7 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  *   bytes 512..639  the 64 rotary values k^R, bf16, unchanged
  *   bytes 640..643  the scale 2^e as a float32;  bytes 644..655 zero
  * The cache then holds code value x 2^e, exact in bf16, and every kernel reads those values.
- * Honoured by mla_decode_partial(_balanced), mla_prefill_chunk (through the bf16 MFMA kernels for
+ * Honoured by mla_decode_partial(_balanced, _grouped), mla_prefill_chunk (through the MFMA kernels for
  * d_c 512, d_r 64, 128 heads) and mla_kv_append (its MFMA path); elsewhere, or for other shapes,
  * the calls return MLA_ERR_UNSUPPORTED.  Latent rows whose largest magnitude is below 2^-110 are
  * outside the supported range (their scale would leave the float32 normal range). */
