@@ -249,10 +249,11 @@ def _run_grouped(inp, n_units, group, q_hat_np, flags=0):
 # verify-style groups (lengths base+1 .. base+G) and unrelated lengths, empty rows included
 GROUP_LENS = {2: [0, 1, 63, 64, 64, 65, 1000, 1025, 0, 0, 3000, 31, 500, 501, 32, 1],
               4: [62, 63, 64, 65, 0, 1, 2, 3, 1022, 1023, 1024, 1025, 0, 0, 0, 0, 3000, 31, 33, 129]}
+GROUP_LENS[20] = GROUP_LENS[4]  # the whole batch as one group
 
 
 @pytest.mark.parametrize("flags", PATHS)
-@pytest.mark.parametrize("group,n_units", [(2, 2), (2, 16), (4, 4), (4, 16), (4, 256)])
+@pytest.mark.parametrize("group,n_units", [(2, 2), (2, 16), (4, 4), (4, 16), (4, 256), (20, 20), (20, 60)])
 def test_count_grouped(group, n_units, flags):
     """Zero query: every segment slot of the grouped split holds its exact token count, and each
     row's merged lse its length."""
