@@ -295,6 +295,30 @@ def test_spike_grouped(n_units, flags):
         assert np.allclose(lse[b], 128.0 * np.log(2.0), atol=1e-4), (L, t, lse[b, :2])
 
 
+@pytest.mark.parametrize("flags", PATHS)
+def test_poison_bitwise_grouped(flags):
+    """NaN / Inf / zero in every cache slot past the rows' ends and in the spare pages give
+    bitwise-identical grouped partials, merges and outputs (row groups of 4, verify-style and
+    unrelated lengths)."""
+    lens = np.array([62, 63, 64, 65, 1, 2, 3, 4, 1200, 31, 4000, 0], np.int32)
+    note(f"poison grouped flags={flags}")
+    outs = []
+    for fill in ("zero", "nan", "inf"):
+        inp = gen.make_decode_inputs(_w(len(lens)), lens=lens, fill=fill, spare_pages=16)
+        st = runner.DecodeStep(inp, 0, DEV, flags=flags, n_units=8)
+        st.absorb()
+        M.mla_decode_partial_grouped(st.d, st.c, st.q_hat, 8, 4, st.ws, st.ws_bytes)
+        M.mla_combine_grouped(st.d, st.c, 8, 4, st.ws, st.ws_bytes, st.z, st.lse)
+        st.out_proj()
+        torch.cuda.synchronize()
+        idx = [sg[4] for sg in segments(lens, 8, group=4)]
+        outs.append([_np(st.o_part)[idx].copy(), _np(st.lse_part)[idx].copy()] +
+                    [_np(x).copy() for x in (st.z, st.lse, st.out)])
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_long_segment_page_windows():
     """Segments longer than 64 pages move the page-id window inside the tile loop; with a spike
     near the end the rerun pass restarts from the first window.  Page size 32 (one tile per
