@@ -28,8 +28,10 @@
 // values stream into LDS in 32-token tiles through direct global-to-LDS transfers, three tiles in
 // flight.  Scores are computed transposed, S^T = [K | k^R] . Q^T (tokens on M, queries on N, 12 k-steps), so every
 // lane holds 16 scores of one query and the softmax stays in the lane plus one v_permlane32_swap.
-// Online softmax with a running maximum; the accumulator is rescaled by a factor that is 1 where
-// the query's maximum stayed (branch-free).
+// Online softmax against a per-query reference that may trail the running maximum by up to 8
+// (base 2): probabilities are taken times 2^7 relative to it (at most 2^15, inside binary16), and
+// the accumulator is rescaled only when some query's maximum climbs further, behind a branch that
+// is uniform over the wave and after the first tiles rarely taken.
 // The weighted sum is accumulated transposed, O^T += V^T . P^T, with V^T from transposing reads in
 // the token order of the score layout.  Output o [b][q][h][128] float32 and lse [b][q][h].
 
@@ -257,7 +259,8 @@ constexpr int kTileRB = kAtT * kDr * 2;      // 4 KiB of k^R
 constexpr int kTileB = 2 * kTileKB + kTileRB;  // K | V | k^R: 20 KiB
 constexpr int kAtBuf = 4;                      // LDS tile buffers: one in use, three in flight
 constexpr int kAtXfer = kTileB / 1024 / 4;     // 5 one-KiB transfers per wave per tile
-constexpr float kPShift = 15.f;                // log2 of the probability scale
+constexpr float kPShift = 7.f;                 // log2 of the probability scale
+constexpr float kLag = 8.f;                     // the reference may trail a query's maximum by this much
 
 // K, V and k^R tile rows use the swizzles of the decompression section above.
 
@@ -415,19 +418,24 @@ __global__ __launch_bounds__(256, 2) void attend_unabsorbed_kernel(
         const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
       }
-      // rescale the running sums by exp2(old max - new max), branch-free (factor 1 where the
-      // maximum stayed, -inf included when no key is visible yet): a conditional rescale made the
-      // compiler copy the accumulators around the branch every tile
+      // the reference m_run moves (and the running sums are rescaled by exp2(old - new)) only
+      // where a query's maximum climbs more than kLag above it, which after the first tiles is
+      // rare: the rescale is skipped when no lane of the wave needs it (a uniform branch), and
+      // inside it the factor is 1 for the other lanes (-inf: no key visible yet)
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
-      l_lane *= alpha;
+      const bool move = m_new > m_run + kLag;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
+        l_lane *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
-      m_run = m_new;
-      // probabilities times 2^kPShift (at most 2^15, inside binary16), so that weights far below
-      // the maximum stay normal numbers; the factor cancels in out and is taken off lse
+          for (int x = 0; x < 16; ++x) acc[db][x] *= alpha;
+        m_run = move ? m_new : m_run;
+      }
+      // probabilities times 2^kPShift relative to the reference: at most 2^(kPShift + kLag) =
+      // 2^15, inside binary16, and weights far below the maximum stay normal numbers; the factor
+      // cancels in out and is taken off lse
       float p[16], tsum = 0.f;
       const float m_use = (m_run == -INFINITY ? 0.f : m_run) - kPShift;  // (no visible key yet: 0)
 #pragma unroll
