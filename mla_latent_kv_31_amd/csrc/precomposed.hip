@@ -15,9 +15,10 @@
 // A bf16 or float32 (split into bf16 hi + lo parts, two MFMAs, about 16 significant bits).  A
 // workgroup of four waves owns 64 rows x 128 columns (wave w: columns 32w..32w+31, both 32-row
 // blocks) and walks its K range in chunks of 64: the chunk of A (64 x 64) and of B (64 x 128) is
-// loaded into registers one chunk ahead, then stored to LDS (double-buffered); A operands are
-// read row-wise, B operands with the transposing ds_read_b64_tr_b16.  Reads of A are shared by the
-// 128 columns of a workgroup; B, the weight, is read from HBM exactly once over the grid.
+// loaded into registers one chunk ahead (every load instruction covering whole rows), then stored
+// to LDS (double-buffered); A operands are read row-wise, B operands with the transposing
+// ds_read_b64_tr_b16.  Reads of A are shared by the 128 columns of a workgroup; B, the weight,
+// is read from HBM exactly once over the grid.
 
 #include <math.h>
 
@@ -33,6 +34,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 64, kTN = 128, kKC = 64;  // workgroup tile and K chunk
 constexpr int kThreads = 256;
@@ -52,12 +56,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
   const int64_t k_begin = int64_t(blockIdx.z) * k_per_split;
   const int nchunks = k_per_split / kKC;
 
-  // global -> register staging of one chunk.  B: 64 k rows x 256 bytes, thread t moves the
-  // 16-byte pieces t + 256x (k row p/16, piece p%16), x < 4.  A: 64 rows x 64 k; thread t moves row
-  // t/4, k 16(t%4) .. +15 (bf16: two 16-byte loads; float32: four).
+  // global -> register staging of one chunk; every load instruction reads whole rows.  B: 64 k
+  // rows x 256 bytes, thread t moves the 16-byte pieces t + 256x (k row p/16, piece p%16), x < 4.
+  // A: 64 rows x 64 k; bf16: thread t moves rows 32x + t/8 (x < 2), bytes 16(t%8) .. +15 of the
+  // row's 128; float32: rows 16x + t/16 (x < 4), floats 4(t%16) .. +3 of the row's 64.
+  constexpr int kAPer = AF32 ? 4 : 2;
+  constexpr int kARowStep = kTM / kAPer, kAThrPerRow = kThreads / kARowStep;
   u32x4 sb[4];
-  u32x4 sa[AF32 ? 4 : 2];
-  const int arow = min(m0 + (t >> 2), M - 1);  // rows past M are computed but never stored
+  u32x4 sa[kAPer];
   auto load = [&](int c) {
     const int64_t k0 = k_begin + int64_t(c) * kKC;
 #pragma unroll
@@ -65,14 +71,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
       const int p = t + kThreads * x;
       sb[x] = *reinterpret_cast<const u32x4*>(b + (k0 + (p >> 4)) * ldb + n0 + 8 * (p & 15));
     }
-    if constexpr (AF32) {
-      const float* a = static_cast<const float*>(a_ptr) + arow * lda + k0 + 16 * (t & 3);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) sa[x] = *reinterpret_cast<const u32x4*>(a + 4 * x);
-    } else {
-      const uint16_t* a = static_cast<const uint16_t*>(a_ptr) + arow * lda + k0 + 16 * (t & 3);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) sa[x] = *reinterpret_cast<const u32x4*>(a + 8 * x);
+    for (int x = 0; x < kAPer; ++x) {
+      const int64_t row = min(m0 + kARowStep * x + t / kAThrPerRow, M - 1);  // rows past M: computed, never stored
+      if constexpr (AF32)
+        sa[x] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(a_ptr) + row * lda + k0 + 4 * (t % kAThrPerRow));
+      else
+        sa[x] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a_ptr) + row * lda + k0 + 8 * (t % kAThrPerRow));
     }
   };
   // LDS layout of a buffer: B [64 k][128 n] bf16 (256-byte rows, 16-byte chunk c of k row k at
@@ -80,38 +85,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const void* __restrict__
   // groups); A hi and A lo [64 m][64 k] bf16 (128-byte rows, chunk c of row r at c ^ ((r >> 1) & 7):
   // 16 consecutive rows at one logical chunk, two rows per 256-byte bank line, hit 16 bank groups)
   auto a_chunk_off = [](int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); };
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
   auto store = [&](int buf) {
     lds_u8* const bb = lbase + buf * kBufB;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int p = t + kThreads * x, k = p >> 4;
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + 256 * k + 16 * ((p & 15) ^ (4 * (k & 3)))) =
-          sb[x];
+      *reinterpret_cast<lds_u32x4*>(bb + 256 * k + 16 * ((p & 15) ^ (4 * (k & 3)))) = sb[x];
     }
-    const int r = t >> 2;
-    if constexpr (AF32) {
-      // 16 floats -> 16 bf16 hi (round to nearest) and 16 bf16 lo (the rounded remainder)
-      u32x4 hi[2], lo[2];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float f0 = __uint_as_float(sa[q >> 1][2 * (q & 1)]), f1 = __uint_as_float(sa[q >> 1][2 * (q & 1) + 1]);
-        const uint16_t h0 = f32_to_bf16(f0), h1 = f32_to_bf16(f1);
-        const uint16_t l0 = f32_to_bf16(f0 - bf16_to_f32(h0)), l1 = f32_to_bf16(f1 - bf16_to_f32(h1));
-        hi[q >> 2][q & 3] = uint32_t(h0) | (uint32_t(h1) << 16);
-        lo[q >> 2][q & 3] = uint32_t(l0) | (uint32_t(l1) << 16);
+    for (int x = 0; x < kAPer; ++x) {
+      const int r = kARowStep * x + t / kAThrPerRow;
+      if constexpr (AF32) {
+        // four floats -> four bf16 hi (round to nearest even) and four bf16 lo (the rounded
+        // remainder, exact in float32): half h = t%2 of logical chunk (t%16)/2 of row r
+        const int q = t & 15, c = q >> 1, h = q & 1;
+        u32x2 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float f0 = __uint_as_float(sa[x][2 * e]), f1 = __uint_as_float(sa[x][2 * e + 1]);
+          const uint32_t hv = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f0, f1}, bf16x2));
+          const float r0 = f0 - __uint_as_float(hv << 16), r1 = f1 - __uint_as_float(hv & 0xffff0000u);
+          hi[e] = hv;
+          lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+        }
+        *reinterpret_cast<lds_u32x2*>(bb + kBChunkB + a_chunk_off(r, c) + 8 * h) = hi;
+        *reinterpret_cast<lds_u32x2*>(bb + kBChunkB + kAChunkB + a_chunk_off(r, c) + 8 * h) = lo;
+      } else {
+        *reinterpret_cast<lds_u32x4*>(bb + kBChunkB + a_chunk_off(r, t % kAThrPerRow)) = sa[x];
       }
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int c = 2 * (t & 3) + x;
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + kBChunkB + a_chunk_off(r, c)) = hi[x];
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + kBChunkB + kAChunkB + a_chunk_off(r, c)) =
-            lo[x];
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(bb + kBChunkB + a_chunk_off(r, 2 * (t & 3) + x)) =
-            sa[x];
     }
   };
 
@@ -265,12 +268,15 @@ __global__ void copy_qr_kernel(const uint16_t* __restrict__ w_qr, int d_cq, int 
   w_qcat[(int64_t(q) * H + h) * (d_c + d_r) + d_c + rr] = w_qr[idx];
 }
 
+// K splits of a product: the most that divide its chunks and keep the grid within 512 workgroups,
+// i.e. one round at two workgroups per CU (64 KiB of LDS each); a second round of short
+// workgroups left the matrix weight stream idle at every start.
 int gemm_splits(int64_t n_total, int M, int64_t K) {
   const int64_t tiles = (n_total / kTN) * ((M + kTM - 1) / kTM);
   const int64_t chunks = K / kKC;
   int best = 1;
   for (int s = 1; s <= 64; ++s)
-    if (chunks % s == 0 && tiles * s <= 1024) best = s;
+    if (chunks % s == 0 && tiles * s <= 512) best = s;
   return best;
 }
 
