@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark: MLA decode over a latent cache on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--split-tokens T | --units N]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--split-tokens T | --units N] [--fused]
 
 A step is one pass of the whole decode hot path over one batch of synthetic
 DeepSeek-V3-shaped input already resident in HBM:
     mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced -> mla_out_proj
 by default (work-balanced split over the compute units), or with --split-tokens T
-the fixed-chunk pair mla_decode_partial -> mla_combine.
+the fixed-chunk pair mla_decode_partial -> mla_combine.  --fused runs the split-K merge and
+the value projection as one call (mla_combine_out_proj_balanced / mla_combine_out_proj).
 W untimed warm-up steps, then exactly K timed steps bracketed by device
 synchronisation.  Prints one JSON line.
 
@@ -713,6 +714,8 @@ def main() -> int:
     ap.add_argument("--split-tokens", type=int, default=None,
                     help="fixed split-K chunks of this many tokens instead of the balanced split")
     ap.add_argument("--units", type=int, default=None, help="units of the balanced split (default: one per CU)")
+    ap.add_argument("--fused", action="store_true",
+                    help="decode step with the fused merge + value projection instead of mla_combine* then mla_out_proj")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="launch one plain device copy of this many MiB first (counter calibration)")
@@ -782,11 +785,12 @@ def main() -> int:
         del src
         inp_dev = dict(inp, pool=pool8)
         flags = L.MLA_FLAG_CACHE_FP8
+    fused = args.fused
     if args.split_tokens:
-        st = runner.DecodeStep(inp_dev, args.split_tokens, dev, flags=flags)
+        st = runner.DecodeStep(inp_dev, args.split_tokens, dev, flags=flags, fused=fused)
     else:
         n_units = args.units or runner.balanced_units(inp["lens"], runner.compute_units(dev))
-        st = runner.DecodeStep(inp_dev, 0, dev, n_units=n_units, flags=flags)
+        st = runner.DecodeStep(inp_dev, 0, dev, n_units=n_units, flags=flags, fused=fused)
     lens = inp["lens"].astype(np.int64)
     total_tokens = int(lens.sum())
     row_bytes = L.MLA_FP8_ROW_BYTES if args.fp8 else (w.d_c + w.d_r) * 2
@@ -826,8 +830,7 @@ def main() -> int:
         ev[i][0].record(stream)
         st.attend()
         ev[i][1].record(stream)
-        st.combine()
-        st.out_proj()
+        st.finish()
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -836,6 +839,28 @@ def main() -> int:
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     ms_decode = float(np.mean(launch_ms))
     copy_gbs = copy["gbs"]
+    # After the timed region: the part after the decode both ways on the same partials, the fused
+    # merge + value projection and mla_combine* followed by mla_out_proj (median of 50 each).
+    finish = None
+    if L.mla_combine_out_proj_supported(st.d):
+        def _median_ms(fn, n=50):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a_, b_ in evs:
+                a_.record(stream)
+                fn()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([a_.elapsed_time(b_) for a_, b_ in evs]))
+
+        def _unfused():
+            st.combine()
+            st.out_proj()
+
+        ms_f = _median_ms(st.combine_out_proj)
+        ms_u = _median_ms(_unfused)
+        finish = {"fused_ms": round(ms_f, 6), "combine_then_out_proj_ms": round(ms_u, 6),
+                  "note": "median time of the calls after the decode launch, on the same partials: the fused "
+                          "merge + value projection against mla_combine* then mla_out_proj"}
 
     sha = _kernel_sha()
     traffic = None if args.fp8 else _traffic(w.name, sha)
@@ -867,9 +892,12 @@ def main() -> int:
                       "work": f"before the warm-up steps: the copy-bandwidth probe ({copy['copies']} plain 1 GiB "
                               f"device copies), then the graph-replay measurement ({n_graph} replays of the same step); "
                               "from idle the board needs about 100 decode steps of load before its clocks settle"},
+        "step_calls": ("absorb, decode, fused merge + value projection" if st.fused
+                       else "absorb, decode, merge, value projection"),
+        "after_decode": finish,
         "graph": {"ms_per_step": round(ms_graph, 6), "value": round(cache_bytes / (ms_graph * 1e-3) / 1e9, 3),
                   "tokens_per_s": round(w.batch / (ms_graph * 1e-3), 1), "replays": n_graph,
-                  "note": "the same four launches captured in one HIP graph and replayed"},
+                  "note": "the same launches captured in one HIP graph and replayed"},
         "roofline": {"bound": "hbm", "kernel": "mla_decode_partial", "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "ms_per_launch": round(ms_decode, 6),

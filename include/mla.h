@@ -240,6 +240,32 @@ mla_status mla_combine_grouped(const mla_dims* dims, const mla_cache* cache, int
 mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, int32_t rows, float* out,
                         void* stream);
 
+/* Split-K merge and value projection in one call: for every row b and head h,
+ *   out[b,h,:] = (sum_i exp(lse_i - LSE) o_i) . W_UV[h],   LSE = ln sum_i exp(lse_i)
+ * over the slots i of row b, i.e. mla_combine* followed by mla_out_proj ([ase] Fig. 2 softmax
+ * merged piecewise, then the Fig. 4 value projection applied once after the weighted sum), with
+ * the merged latent z kept on chip instead of written and read back.  Results equal those of the
+ * two calls up to the order of floating-point summation.  A row with no key gives out = 0,
+ * lse = -inf.  Only the DeepSeek-V3 shape in bf16 is implemented (d_c 512, d_k = d_v 128, d_r a
+ * multiple of 8 up to 64): mla_combine_out_proj_supported(dims) says whether dims qualify (0 also
+ * for invalid dims or MLA_FLAG_FORCE_GENERIC); otherwise every variant returns
+ * MLA_ERR_UNSUPPORTED and the caller runs the two calls.
+ *   workspace, workspace_bytes  the partials as mla_decode_partial (mla_combine_out_proj: batch,
+ *            n_splits) or mla_decode_partial_balanced / _grouped (same n_units, row_group) wrote
+ *            them; MLA_ERR_WORKSPACE when below the size the matching merge call requires
+ *   w_uv     device bf16 [H, d_c, d_v]
+ *   out      device float [batch, H, d_v]   (output)
+ *   lse      device float [batch, H] or NULL (output, natural log)                              */
+int32_t mla_combine_out_proj_supported(const mla_dims* dims);
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t n_splits, const void* workspace,
+                                size_t workspace_bytes, const void* w_uv, float* out, float* lse, void* stream);
+mla_status mla_combine_out_proj_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                         const void* workspace, size_t workspace_bytes, const void* w_uv, float* out,
+                                         float* lse, void* stream);
+mla_status mla_combine_out_proj_grouped(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                        int32_t row_group, const void* workspace, size_t workspace_bytes,
+                                        const void* w_uv, float* out, float* lse, void* stream);
+
 /* Causal multi-query attention for a chunk of new tokens whose rows are already in the cache
  * ([ase] causal-mask remark after Fig. 2; [molayo] chunked prefill).  Query i of sequence b sits
  * at absolute position q_start[b] + i and reads tokens t <= q_start[b] + i, t < seq_lens[b].

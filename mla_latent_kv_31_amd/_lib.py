@@ -77,6 +77,10 @@ _SIGNATURES = {
     "mla_decode_partial_grouped": (_I32, [_PD, _PC, _VP, _I32, _I32, _VP, ctypes.c_size_t, _VP]),
     "mla_combine_grouped": (_I32, [_PD, _PC, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_out_proj": (_I32, [_PD, _VP, _VP, _I32, _VP, _VP]),
+    "mla_combine_out_proj_supported": (_I32, [_PD]),
+    "mla_combine_out_proj": (_I32, [_PD, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP]),
+    "mla_combine_out_proj_balanced": (_I32, [_PD, _PC, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP]),
+    "mla_combine_out_proj_grouped": (_I32, [_PD, _PC, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP]),
     "mla_prefill_chunk": (_I32, [_PD, _PC, _VP, _I32, _VP, _VP, _VP, _VP]),
     "mla_project_query": (_I32, [_PD, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
     "mla_decompress_kv": (_I32, [_PD, _PC, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
@@ -245,6 +249,31 @@ def mla_combine_grouped(d: MlaDims, c: MlaCache, n_units: int, row_group: int, w
 def mla_out_proj(d: MlaDims, z, w_uv, rows: int, out, stream=None) -> None:
     _check(library().mla_out_proj(ctypes.byref(d), _addr(z), _addr(w_uv), rows, _addr(out), _stream(stream)),
            "mla_out_proj")
+
+
+def mla_combine_out_proj_supported(d: MlaDims) -> bool:
+    return bool(library().mla_combine_out_proj_supported(ctypes.byref(d)))
+
+
+def mla_combine_out_proj(d: MlaDims, batch: int, n_splits: int, workspace, workspace_bytes: int, w_uv, out,
+                         lse=None, stream=None) -> None:
+    _check(library().mla_combine_out_proj(ctypes.byref(d), batch, n_splits, _addr(workspace), workspace_bytes,
+                                          _addr(w_uv), _addr(out), _addr(lse), _stream(stream)),
+           "mla_combine_out_proj")
+
+
+def mla_combine_out_proj_balanced(d: MlaDims, c: MlaCache, n_units: int, workspace, workspace_bytes: int, w_uv, out,
+                                  lse=None, stream=None) -> None:
+    _check(library().mla_combine_out_proj_balanced(ctypes.byref(d), ctypes.byref(c), n_units, _addr(workspace),
+                                                   workspace_bytes, _addr(w_uv), _addr(out), _addr(lse),
+                                                   _stream(stream)), "mla_combine_out_proj_balanced")
+
+
+def mla_combine_out_proj_grouped(d: MlaDims, c: MlaCache, n_units: int, row_group: int, workspace,
+                                 workspace_bytes: int, w_uv, out, lse=None, stream=None) -> None:
+    _check(library().mla_combine_out_proj_grouped(ctypes.byref(d), ctypes.byref(c), n_units, row_group,
+                                                  _addr(workspace), workspace_bytes, _addr(w_uv), _addr(out),
+                                                  _addr(lse), _stream(stream)), "mla_combine_out_proj_grouped")
 
 
 def mla_prefill_chunk(d: MlaDims, c: MlaCache, q_hat, q_len: int, q_start, z, lse=None, stream=None) -> None:

@@ -303,6 +303,55 @@ mla_status mla_out_proj(const mla_dims* dims, const float* z, const void* w_uv, 
   return hip_status(launch_out_proj_generic(d, z, w_uv, rows, out, (hipStream_t)stream));
 }
 
+int32_t mla_combine_out_proj_supported(const mla_dims* dims) {
+  Dims d;
+  if (check_dims(dims, &d) != MLA_OK || generic_forced(dims)) return 0;
+  return proj_mfma_supported(d) ? 1 : 0;
+}
+
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t n_splits, const void* workspace,
+                                size_t workspace_bytes, const void* w_uv, float* out, float* lse, void* stream) {
+  Dims d;
+  Partials p;
+  MLA_TRY(check_dims(dims, &d));
+  if (batch < 0 || n_splits < 1) return MLA_ERR_SHAPE;
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  if (!mla_combine_out_proj_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(check_workspace(d, int64_t(batch) * n_splits, workspace, workspace_bytes, &p));
+  MLA_TRY(ptr_ok(w_uv));
+  MLA_TRY(ptr_ok(out));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (batch == 0) return MLA_OK;
+  return hip_status(
+      launch_combine_out_proj(d, nullptr, batch, n_splits, 1, p.o, p.lse, w_uv, out, lse, (hipStream_t)stream));
+}
+
+mla_status mla_combine_out_proj_grouped(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                        int32_t row_group, const void* workspace, size_t workspace_bytes,
+                                        const void* w_uv, float* out, float* lse, void* stream) {
+  Dims d;
+  Cache c;
+  Partials p;
+  MLA_TRY(check_dims(dims, &d));
+  MLA_TRY(check_cache(cache, &c));
+  MLA_TRY(check_balanced(c, n_units));
+  MLA_TRY(check_group(c, n_units, row_group));
+  if (!mla_combine_out_proj_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  MLA_TRY(check_workspace(d, mla_balanced_num_slots(c.batch, n_units), workspace, workspace_bytes, &p));
+  MLA_TRY(ptr_ok(w_uv));
+  MLA_TRY(ptr_ok(out));
+  if (lse && !(reinterpret_cast<uintptr_t>(lse) % 16 == 0)) return MLA_ERR_ALIGN;
+  if (c.batch == 0) return MLA_OK;
+  return hip_status(launch_combine_out_proj(d, &c, c.batch, n_units, row_group, p.o, p.lse, w_uv, out, lse,
+                                            (hipStream_t)stream));
+}
+
+mla_status mla_combine_out_proj_balanced(const mla_dims* dims, const mla_cache* cache, int32_t n_units,
+                                         const void* workspace, size_t workspace_bytes, const void* w_uv, float* out,
+                                         float* lse, void* stream) {
+  return mla_combine_out_proj_grouped(dims, cache, n_units, 1, workspace, workspace_bytes, w_uv, out, lse, stream);
+}
+
 mla_status mla_prefill_chunk(const mla_dims* dims, const mla_cache* cache, const void* q_hat, int32_t q_len,
                              const int32_t* q_start, float* z, float* lse, void* stream) {
   Dims d;

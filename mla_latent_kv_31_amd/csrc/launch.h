@@ -52,6 +52,11 @@ hipError_t launch_combine_fast(const Dims& d, int batch, int n_splits, const flo
                                float* z, float* lse, hipStream_t s);
 hipError_t launch_combine_fast_balanced(const Dims& d, const Cache& c, int n_units, int group, const float* o_part,
                                         const float* lse_part, float* z, float* lse, hipStream_t s);
+// split-K merge fused with the value projection (proj_mfma.hip; proj_mfma_supported shapes): c is the
+// cache of the balanced split (S = n_units, row groups of `group`), or NULL for the fixed split
+// (S = n_splits)
+hipError_t launch_combine_out_proj(const Dims& d, const Cache* c, int batch, int S, int group, const float* o_part,
+                                   const float* lse_part, const void* w_uv, float* out, float* lse, hipStream_t s);
 
 hipError_t launch_absorb_generic(const Dims& d, const void* q_c, const void* q_r, const void* w_uk,
                                  const int32_t* pos, int rows, void* q_hat, hipStream_t s);

@@ -16,11 +16,16 @@
 // 32 or 64 rows); beyond that one workgroup per (head, 64 value columns) streams every row slice.
 // z is float32: it is split into bf16 hi + lo parts and both are multiplied (two MFMAs), which
 // keeps the product at float32-level accuracy.
+//
+// mla_combine_out_proj (+ _balanced, _grouped): the split-K log-sum-exp merge and the value
+// projection in one kernel, out = (sum_i exp(lse_i - LSE) o_i) . W_UV[h], with the same product as
+// mla_out_proj and the merged latent kept in registers.
 
 #include <math.h>
 
 #include "common.h"
 #include "launch.h"
+#include "schedule.h"
 
 namespace mla {
 namespace {
@@ -439,6 +444,210 @@ __global__ __launch_bounds__(256) void out_proj_stream_kernel(int H, int R, cons
   }
 }
 
+// ------------------------------------------------------------------- split-K merge + out_proj
+// out[b,h,:] = (sum_i exp(lse_i - LSE) o_i) . W_UV[h], LSE = ln sum_i exp(lse_i), over the split-K
+// slots i of row b ([ase] Fig. 2 softmax merged piecewise, then the Fig. 4 value projection): the
+// merge of mla_combine_* and the product of mla_out_proj in one pass, so that the merged latent z
+// never goes through memory.  One workgroup of eight waves per (head h, 32 rows), all 128 value
+// columns; the workgroups of a head sit on its XCD, which fetches W_UV[h] from HBM once.  Wave w
+// owns the contraction slice j = 64w .. 64w + 63: its W_UV rows (16 KiB) stream into its own LDS
+// by direct global-to-LDS transfers while the wave merges, for row r0 + lane % 32, the 32 values
+// z[j0 + 16ks + 8hi .. +7] (ks = 0..3) over that row's slots, four slots' loads in flight (the
+// first four issued together with the log-sum-exp loads, before the weights are known).  The
+// merged values are split into bf16 hi + lo parts and multiplied as in out_proj; the eight
+// slices' sums meet in LDS.  Slots of zero weight (empty chunks, never written) are loaded but
+// dropped by a select, so whatever bits they hold never reach the output.
+constexpr int kCpRows = 32;                 // rows per workgroup
+constexpr int kCpWaves = 8;
+constexpr int kCpJ = kDc / kCpWaves;        // 64 contraction rows per wave
+constexpr int kCpKs = kCpJ / 16;            // 4 MFMA k-steps per wave
+constexpr int kCpSlots = 3;                 // slots per load round
+constexpr int kCpRowB = kDv * 2;            // 256 bytes: one W_UV row in LDS
+constexpr int kCpWaveB = kCpJ * kCpRowB;    // 16 KiB: a wave's W_UV rows, later its partial sums
+
+// LDS chunk position of 16-byte chunk c of W_UV row j (j taken within a wave's rows): the
+// 4-row x 32-byte transposing reads then fall into four different 32-byte bank groups.
+__device__ __forceinline__ int cp_chunk(int j, int c) { return c ^ (2 * (j & 3)); }
+
+__device__ __forceinline__ void cp_dma16(uint32_t lds_dst, uint32_t voff, const unsigned char* gbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase)
+               : "memory");
+}
+
+// kBalanced: S = n_units and `group` the row-group size of the balanced split (schedule.h);
+// otherwise S = n_splits and row b's slots are b*S .. b*S+S-1.
+template <bool kBalanced>
+__global__ __launch_bounds__(64 * kCpWaves) void combine_out_proj_kernel(
+    int H, int S, int group, const int32_t* __restrict__ seq_lens, int batch, int cap,
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, const uint16_t* __restrict__ w_uv,
+    float* __restrict__ out, float* __restrict__ lse_out) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kCpWaves * kCpWaveB];  // 128 KiB
+  int h, inner;
+  if (!xcd_head_map((batch + kCpRows - 1) / kCpRows, H, h, inner)) return;
+  // the wave index as a wave-uniform value: the transfer addresses below live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, hi = lane >> 5, g = lane >> 4, ii = lane & 15;
+  const int j0 = kCpJ * wave;
+  lds_u8* const lw = (lds_u8*)smem + wave * kCpWaveB;
+
+  // ---- the slots of row r: base, base + step, ... (count of them)
+  const int r = kCpRows * inner + (lane & 31);
+  const bool valid = r < batch;
+  const int b = valid ? r : batch - 1;
+  int base = b * S, count = valid ? S : 0, step = 1;
+  if constexpr (kBalanced) {
+    const int n_groups = batch / group, grp = b / group, gi = b - grp * group;
+    const int tiles = sched_tiles(sched_len(seq_lens[b], cap));  // this row's own tiles
+    // cost prefix of this lane's group and the total cost, in one wave-wide scan over the groups
+    int total = 0, cb = 0;
+    for (int c0 = 0; c0 < n_groups; c0 += 64) {
+      const int i = c0 + lane;
+      const int c = i < n_groups ? sched_cost(sched_group_len(seq_lens, i, group, cap)) : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int src = grp - c0;
+      const int ex = __shfl(incl - c, src & 63, 64);
+      if (src >= 0 && src < 64) cb = total + ex;
+      total += __shfl(incl, 63, 64);
+    }
+    base = 0;
+    count = 0;
+    if (valid && tiles > 0) {
+      int w0, w1;
+      sched_units(cb, tiles, sched_quota(total, S / group), w0, w1);
+      base = sched_slot(w0, grp, group, gi);
+      count = w1 - w0 + 1;
+      step = group;
+    }
+  }
+  int maxc = count;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) maxc = max(maxc, __shfl_xor(maxc, o, 64));
+  const float* lp = lse_part + size_t(base) * H + h;
+  const size_t lstride = size_t(step) * H;
+  const float* op = o_part + (size_t(base) * H + h) * kDc + j0 + 8 * hi;
+  const size_t ostride = size_t(step) * H * kDc;
+
+  // one round: the lse and z pieces of slots s0 .. s0 + kCpSlots - 1 (clamped to the row's last
+  // slot, so that every load stays inside the row's own slots)
+  f32x4 x[kCpSlots][kCpKs][2];
+  float xl[kCpSlots];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < kCpSlots; ++k) {
+      const int s = min(s0 + k, max(count - 1, 0));
+      xl[k] = lp[s * lstride];
+      const float* p = op + s * ostride;
+#pragma unroll
+      for (int ks = 0; ks < kCpKs; ++ks) {
+        x[k][ks][0] = *reinterpret_cast<const f32x4*>(p + 16 * ks);
+        x[k][ks][1] = *reinterpret_cast<const f32x4*>(p + 16 * ks + 4);
+      }
+    }
+  };
+  load_round(0);
+
+  // ---- this wave's W_UV rows, in flight while the slots are merged: 16 transfers of four 256-byte
+  // rows; lane L fills LDS chunk L % 16 of row 4t + L / 16 with the global chunk cp_chunk places there
+  {
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(w_uv + (size_t(h) * kDc + j0) * kDv);
+    const uint32_t dst = uint32_t(reinterpret_cast<uintptr_t>(lw));
+    const uint32_t voff = uint32_t(kCpRowB * g + 16 * cp_chunk(g, ii));
+#pragma unroll
+    for (int t = 0; t < kCpJ / 4; ++t) cp_dma16(dst + 1024u * t, voff, src + size_t(1024) * t);
+  }
+
+  // ---- log-sum-exp weights of the row's slots (the first eight loaded at once)
+  constexpr int kL = 8;
+  float lv[kL];
+#pragma unroll
+  for (int k = 0; k < kL; ++k) lv[k] = k < count ? lp[k * lstride] : -INFINITY;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kL; ++k) mx = fmaxf(mx, lv[k]);
+  for (int s = kL; s < count; ++s) mx = fmaxf(mx, lp[s * lstride]);
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kL; ++k) tot += k < count ? expf(lv[k] - mx) : 0.f;
+    for (int s = kL; s < count; ++s) tot += expf(lp[s * lstride] - mx);
+  }
+  const float inv = mx != -INFINITY ? 1.f / tot : 0.f;
+  if (lse_out && wave == 0 && hi == 0 && valid)
+    lse_out[size_t(r) * H + h] = mx != -INFINITY ? mx + logf(tot) : -INFINITY;
+
+  // ---- z pieces of this row and contraction slice, merged over the slots
+  f32x4 za[kCpKs][2];
+#pragma unroll
+  for (int ks = 0; ks < kCpKs; ++ks) za[ks][0] = za[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0;;) {
+#pragma unroll
+    for (int k = 0; k < kCpSlots; ++k) {
+      const float wk = s0 + k < count && mx != -INFINITY ? expf(xl[k] - mx) * inv : 0.f;
+      const bool use = wk != 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kCpKs; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) za[ks][e][q] = use ? fmaf(wk, x[k][ks][e][q], za[ks][e][q]) : za[ks][e][q];
+    }
+    s0 += kCpSlots;
+    if (s0 >= maxc) break;
+    load_round(s0);
+  }
+
+  // ---- out^T[v][r] = W_UV^T[v][j] . z^T[j][r] over this wave's slice, as in out_proj
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W_UV rows have landed
+  f32x16 acc[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[vb][e] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kCpKs; ++ks) {
+    bf16x8 zh, zl;
+    split_hilo(za[ks][0], za[ks][1], true, zh, zl);
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+      const int jr = 16 * ks + 8 * (g >> 1) + (ii >> 2), ccol = 32 * vb + 16 * (g & 1) + 4 * (ii & 3);
+      const lds_u8* p0 = lw + jr * kCpRowB + 16 * cp_chunk(jr, ccol >> 3) + 2 * (ccol & 7);
+      const lds_u8* p1 = lw + (jr + 4) * kCpRowB + 16 * cp_chunk(jr + 4, ccol >> 3) + 2 * (ccol & 7);
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+      const bf16x8 aw = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zh, acc[vb], 0, 0, 0);
+      acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, zl, acc[vb], 0, 0, 0);
+    }
+  }
+
+  // ---- the eight slices' sums meet in LDS, each wave's in its own (no longer read) W_UV rows;
+  // wave w < 4 finishes value block w
+  typedef __attribute__((address_space(3))) f32x4 lds_f4;
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(lds_f4*)(lw + (vb * 4 + q) * 1024 + 16 * lane) =
+          f32x4{acc[vb][4 * q], acc[vb][4 * q + 1], acc[vb][4 * q + 2], acc[vb][4 * q + 3]};
+  __syncthreads();
+  if (wave >= 4 || !valid) return;
+  float* o = out + (size_t(r) * H + h) * kDv + 32 * wave + 4 * hi;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kCpWaves; ++w)
+      sum += *(const lds_f4*)((lds_u8*)smem + w * kCpWaveB + (wave * 4 + q) * 1024 + 16 * lane);
+    // D layout: lane holds row lane % 32, v = 8q + 4hi + 0..3 of the 32-column block
+    *reinterpret_cast<f32x4*>(o + 8 * q) = sum;
+  }
+}
+
 }  // namespace
 
 bool proj_mfma_supported(const Dims& d) {
@@ -474,6 +683,18 @@ hipError_t launch_out_proj_mfma(const Dims& d, const float* z, const void* w_uv,
   else  // prefill chunks: one streaming workgroup per (head, column half)
     out_proj_stream_kernel<<<dim3(xcd_grid(kHalves, d.H)), 256, 0, s>>>(d.H, rows, z,
                                                                         static_cast<const uint16_t*>(w_uv), out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_out_proj(const Dims& d, const Cache* c, int batch, int S, int group, const float* o_part,
+                                   const float* lse_part, const void* w_uv, float* out, float* lse, hipStream_t s) {
+  const dim3 grid(xcd_grid((batch + kCpRows - 1) / kCpRows, d.H));
+  const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+  if (c)
+    combine_out_proj_kernel<true><<<grid, 64 * kCpWaves, 0, s>>>(d.H, S, group, c->seq_lens, batch,
+                                                      c->max_pages * c->page_size, o_part, lse_part, w, out, lse);
+  else
+    combine_out_proj_kernel<false><<<grid, 64 * kCpWaves, 0, s>>>(d.H, S, 1, nullptr, batch, 0, o_part, lse_part, w, out, lse);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@ Decode step (one query token per sequence):
     mla_absorb_query -> mla_decode_partial -> mla_combine -> mla_out_proj
 or, with the work-balanced split over ``n_units`` workgroups:
     mla_absorb_query -> mla_decode_partial_balanced -> mla_combine_balanced -> mla_out_proj
+and, with ``fused=True``, the merge and the value projection as one call
+(mla_combine_out_proj / mla_combine_out_proj_balanced; z is then not written).
 Chunked prefill (q_len query tokens per sequence):
     mla_absorb_query -> mla_prefill_chunk -> mla_out_proj
 Multi-token verify (q_len query tokens per sequence, as batch * q_len decode rows):
@@ -82,7 +84,7 @@ class DecodeStep:
     """
 
     def __init__(self, inp: dict, split_tokens: int = 0, device="cuda:0", flags: int = 0,
-                 max_len: int | None = None, n_units: int | None = None):
+                 max_len: int | None = None, n_units: int | None = None, fused: bool = False):
         w = inp["workload"]
         self.w = w
         self.device = torch.device(device)
@@ -119,6 +121,7 @@ class DecodeStep:
         self.lse = torch.empty((self.B, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((self.B, H, w.d_v), dtype=torch.float32, device=dev)
         self.c = L.cache(self.pool, self.page_table, self.lens)
+        self.fused = bool(fused) and L.mla_combine_out_proj_supported(self.d)
 
     def uses_mfma(self) -> bool:
         return L.mla_decode_uses_mfma(self.d, self.c, self.split_tokens)
@@ -142,11 +145,27 @@ class DecodeStep:
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B, self.out, stream)
 
+    def combine_out_proj(self, stream=None):
+        """Merge and value projection in one call (out and lse; z is not written)."""
+        if self.n_units is not None:
+            L.mla_combine_out_proj_balanced(self.d, self.c, self.n_units, self.ws, self.ws_bytes, self.w_uv, self.out,
+                                            self.lse, stream)
+        else:
+            L.mla_combine_out_proj(self.d, self.B, self.S, self.ws, self.ws_bytes, self.w_uv, self.out, self.lse,
+                                   stream)
+
+    def finish(self, stream=None):
+        """Everything after the split-K decode: the fused call, or mla_combine* then mla_out_proj."""
+        if self.fused:
+            self.combine_out_proj(stream)
+        else:
+            self.combine(stream)
+            self.out_proj(stream)
+
     def run(self, stream=None):
         self.absorb(stream)
         self.attend(stream)
-        self.combine(stream)
-        self.out_proj(stream)
+        self.finish(stream)
 
 
 class PrefillStep:
@@ -205,7 +224,8 @@ class VerifyStep:
     ``n_units`` is rounded down to a multiple of q_len for the grouped split.
     Same inputs and outputs as PrefillStep (``out`` [B, q_len, H, d_v], ``lse`` [B, q_len, H])."""
 
-    def __init__(self, inp: dict, device="cuda:0", n_units: int = 256, flags: int = 0, grouped: bool = True):
+    def __init__(self, inp: dict, device="cuda:0", n_units: int = 256, flags: int = 0, grouped: bool = True,
+                 fused: bool = False):
         w = inp["workload"]
         self.w = w
         self.device = torch.device(device)
@@ -238,6 +258,7 @@ class VerifyStep:
         self.c = L.cache(self.pool, self.page_table, self.lens)
         self.rc = L.cache(self.pool, self.row_table, self.row_lens, batch=R, page_size=int(self.pool.shape[1]),
                           max_pages=max_pages, num_pages=int(self.pool.shape[0]))
+        self.fused = bool(fused) and L.mla_combine_out_proj_supported(self.d)
 
     def rows(self, stream=None):
         L.mla_verify_rows(self.c, self.q_start, self.Sq, self.row_table, self.row_lens, self.row_pos, stream)
@@ -256,12 +277,22 @@ class VerifyStep:
     def out_proj(self, stream=None):
         L.mla_out_proj(self.d, self.z, self.w_uv, self.B * self.Sq, self.out, stream)
 
+    def combine_out_proj(self, stream=None):
+        L.mla_combine_out_proj_grouped(self.d, self.rc, self.n_units, self.group, self.ws, self.ws_bytes, self.w_uv,
+                                       self.out, self.lse, stream)
+
+    def finish(self, stream=None):
+        if self.fused:
+            self.combine_out_proj(stream)
+        else:
+            self.combine(stream)
+            self.out_proj(stream)
+
     def run(self, stream=None):
         self.rows(stream)
         self.absorb(stream)
         self.attend(stream)
-        self.combine(stream)
-        self.out_proj(stream)
+        self.finish(stream)
 
 
 class PrefillUnabsorbedStep:

@@ -320,3 +320,44 @@ def test_split_k_workspace_sizes_and_rejection():
     # an empty batch needs no partial bytes
     assert _decode(d, _cache(batch=0), nbytes=0) == M.MLA_OK
     assert M.mla_decode_balanced_workspace_bytes(d, _cache(batch=0), 256) == 0
+
+
+def test_combine_out_proj_validation():
+    """The fused merge + value projection: supported only for the bf16 V3 shape, and rejected on
+    the host like the two calls it replaces (sizes, NULLs, alignment, short workspace)."""
+    lib = M.library()
+    d = _dims()
+    c = _cache()
+    assert M.mla_combine_out_proj_supported(d)
+    assert not M.mla_combine_out_proj_supported(_dims(dtype=M.MLA_F32))
+    assert not M.mla_combine_out_proj_supported(_dims(d_c=256))
+    assert not M.mla_combine_out_proj_supported(_dims(flags=M.MLA_FLAG_FORCE_GENERIC))
+
+    def fixed(dd=d, batch=4, n=256, ws=A, nbytes=BIG, w=A, out=A, lse=None):
+        return lib.mla_combine_out_proj(ctypes.byref(dd), batch, n, ws, nbytes, w, out, lse, None)
+
+    def grouped(cc=c, n=256, g=1, ws=A, nbytes=BIG, w=A, out=A, lse=None, dd=d):
+        return lib.mla_combine_out_proj_grouped(ctypes.byref(dd), ctypes.byref(cc), n, g, ws, nbytes, w, out, lse,
+                                                None)
+
+    assert fixed(n=0) == M.MLA_ERR_SHAPE
+    assert fixed(batch=-1) == M.MLA_ERR_SHAPE
+    assert fixed(batch=70000) == M.MLA_ERR_UNSUPPORTED
+    assert fixed(dd=_dims(dtype=M.MLA_F32)) == M.MLA_ERR_UNSUPPORTED
+    assert fixed(w=None) == M.MLA_ERR_NULL
+    assert fixed(out=U) == M.MLA_ERR_ALIGN
+    assert fixed(lse=U) == M.MLA_ERR_ALIGN
+    assert fixed(ws=None) == M.MLA_ERR_NULL
+    need = M.mla_partials_bytes(d, 4 * 256)
+    assert fixed(nbytes=need - 1) == M.MLA_ERR_WORKSPACE
+    assert fixed(batch=0, nbytes=0) == M.MLA_OK
+    assert grouped(n=0) == M.MLA_ERR_SHAPE
+    assert grouped(g=3) == M.MLA_ERR_SHAPE              # does not divide batch 4
+    assert grouped(cc=_cache(page_size=0)) == M.MLA_ERR_SHAPE
+    assert grouped(dd=_dims(d_v=64)) == M.MLA_ERR_UNSUPPORTED
+    assert grouped(w=None) == M.MLA_ERR_NULL
+    need = M.mla_decode_balanced_workspace_bytes(d, c, 256)
+    assert grouped(nbytes=need - 1) == M.MLA_ERR_WORKSPACE
+    assert lib.mla_combine_out_proj_balanced(ctypes.byref(d), ctypes.byref(c), 256, A, need - 1, A, A, None,
+                                             None) == M.MLA_ERR_WORKSPACE
+    assert grouped(cc=_cache(batch=0), nbytes=0) == M.MLA_OK
