@@ -7,8 +7,9 @@ query tensors are rewritten in place (A, then B, then A). A replay must read its
 never reuse an earlier result. The outputs are filled with NaN before every replay, so each one
 must write them in full.
 
-Covered: the balanced, fixed-split and FP8-cache decode steps, the absorbed and unabsorbed
-prefill calls, and the multi-token verify step.
+Covered: the balanced, fixed-split and FP8-cache decode steps (and the balanced and fixed steps
+with the merge and value projection fused), the absorbed and unabsorbed prefill calls, and the
+multi-token verify step.
 """
 
 import numpy as np
@@ -83,6 +84,22 @@ def test_decode_step_graph(mode):
     else:
         make = lambda i: runner.DecodeStep(i, 0, DEV, flags=flags, n_units=256)  # noqa: E731
     _check_replays(make, inp_a, inp_b, ("out", "z", "lse"))
+
+
+@pytest.mark.parametrize("mode", ["balanced", "fixed"])
+def test_decode_step_graph_fused(mode):
+    """The step whose merge and value projection are one call (mla_combine_out_proj*); z is not
+    written on this path, so out and lse are compared."""
+    inp_a = _decode_inputs(65)
+    q_b = _decode_inputs(66)
+    inp_b = dict(inp_a, q_c=q_b["q_c"], q_r=q_b["q_r"])
+    note(f"graph replays, fused decode {mode}")
+    if mode == "fixed":
+        make = lambda i: runner.DecodeStep(i, 512, DEV, fused=True)  # noqa: E731
+    else:
+        make = lambda i: runner.DecodeStep(i, 0, DEV, n_units=256, fused=True)  # noqa: E731
+    assert make(inp_a).fused
+    _check_replays(make, inp_a, inp_b, ("out", "lse"))
 
 
 @pytest.mark.parametrize("kind", ["prefill", "prefill_unabsorbed", "verify"])
