@@ -193,9 +193,20 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){a, b}, f16x2));
 }
 
+// One 16-byte-per-lane transfer of cached rows into LDS.  bf16 rows (1,152 B, nine whole 128-byte
+// lines) are read once per workgroup, so their transfers carry the non-temporal hint: the streamed
+// cache does not displace the lines that are read again (q_hat and page-table rows of other units,
+// and what the launches after the decode read: the partials, W_UV, W_UK).  FP8 rows (656 B) share
+// lines between the code, rotary and scale transfers of a row and its neighbours, which the hint
+// would evict between those reads, so they are loaded normally.
+template <bool kNT>
 __device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const unsigned char* gbase) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase)
-               : "memory");
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_dst), "v"(voff), "s"(gbase)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(gbase)
+                 : "memory");
 }
 
 // Page ids of 64 consecutive pages of a sequence's table, one per lane, loaded and waited for in
@@ -381,9 +392,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     auto dma_one = [&](const unsigned char* gsrc, uint32_t dst, int x) {  // x-th transfer of a tile
       if (x < kLatPerWave) {
         const int n = 4 * x + wave_u;
-        dma16(dst + uint32_t(n * kLatB), lat_off(x), gsrc + size_t(n) * kRowB);
+        dma16<true>(dst + uint32_t(n * kLatB), lat_off(x), gsrc + size_t(n) * kRowB);
       } else {
-        dma16(dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB);
+        dma16<true>(dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB);
       }
     };
     auto dma_tile = [&](int k) {  // tile min(k, ntiles-1) into buffer k % kNB
@@ -422,13 +433,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
       const uint32_t dst = lds0 + uint32_t(kStgOff + stg * kStgB);
       if (x < 4) {
         const int T = 4 * wave_u + x;
-        dma16(dst + uint32_t(T * 1024), c8_off, gsrc + size_t(2 * T) * kRowB8);
+        dma16<false>(dst + uint32_t(T * 1024), c8_off, gsrc + size_t(2 * T) * kRowB8);
       } else if (wave_u == 0) {
-        dma16(dst + uint32_t(kStgCodesB), s8_off, gsrc);
+        dma16<false>(dst + uint32_t(kStgCodesB), s8_off, gsrc);
       }
     };
     auto dma_rope8 = [&](const unsigned char* gsrc, int k) {
-      dma16(lds0 + uint32_t((k % kNB) * kTileB + kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB8);
+      dma16<false>(lds0 + uint32_t((k % kNB) * kTileB + kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB8);
     };
     auto dma_tile8 = [&](int k) {  // codes and scales of tile k into slot k&1, its rotary rows into buffer k%3
       const unsigned char* gsrc = tile_src(min(k, ntiles - 1));
