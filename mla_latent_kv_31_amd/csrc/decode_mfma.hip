@@ -193,12 +193,12 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){a, b}, f16x2));
 }
 
-// One 16-byte-per-lane transfer of cached rows into LDS.  bf16 rows (1,152 B, nine whole 128-byte
-// lines) are read once per workgroup, so their transfers carry the non-temporal hint: the streamed
-// cache does not displace the lines that are read again (q_hat and page-table rows of other units,
-// and what the launches after the decode read: the partials, W_UV, W_UK).  FP8 rows (656 B) share
-// lines between the code, rotary and scale transfers of a row and its neighbours, which the hint
-// would evict between those reads, so they are loaded normally.
+// One 16-byte-per-lane transfer of cached rows into LDS.  Where a bf16 row (1,152 B, nine whole
+// 128-byte lines) is read by one workgroup only, the transfer carries the non-temporal hint (kNT):
+// the streamed cache then does not displace the lines that are read again (q_hat and page-table
+// rows of other units, and what the launches after the decode read: the partials, W_UV, W_UK).
+// FP8 rows (656 B) share lines between the code, rotary and scale transfers of a row and its
+// neighbours, which the hint would evict between those reads, so they are loaded normally.
 template <bool kNT>
 __device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const unsigned char* gbase) {
   if constexpr (kNT)
@@ -228,7 +228,10 @@ enum Mode {
                   // straight to z / lse; grid = rows, longest rows first
 };
 
-template <int MODE, bool F8>
+// NT: the bf16 tile transfers carry the non-temporal hint; set where each cached row is read by one
+// workgroup only (fixed split, plain balanced split), clear where other workgroups read the same
+// rows shortly after and should find them in L2 (row groups, prefill rows of one sequence).
+template <int MODE, bool F8, bool NT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __restrict__ page_table,
                         const int32_t* __restrict__ seq_lens, int batch, int max_pages, int page_size,
@@ -392,9 +395,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ pool, const int32_t* __rest
     auto dma_one = [&](const unsigned char* gsrc, uint32_t dst, int x) {  // x-th transfer of a tile
       if (x < kLatPerWave) {
         const int n = 4 * x + wave_u;
-        dma16<true>(dst + uint32_t(n * kLatB), lat_off(x), gsrc + size_t(n) * kRowB);
+        dma16<NT>(dst + uint32_t(n * kLatB), lat_off(x), gsrc + size_t(n) * kRowB);
       } else {
-        dma16<true>(dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB);
+        dma16<NT>(dst + uint32_t(kRopeOff + wave_u * 1024), rope_off(), gsrc + size_t(8 * wave_u) * kRowB);
       }
     };
     auto dma_tile = [&](int k) {  // tile min(k, ntiles-1) into buffer k % kNB
@@ -845,7 +848,7 @@ hipError_t launch_decode_mfma(const Dims& d, const Cache& c, const void* q_hat, 
                               float* o_part, float* lse_part, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  auto k = fp8 ? decode_mfma_kernel<kFixed, true> : decode_mfma_kernel<kFixed, false>;
+  auto k = fp8 ? decode_mfma_kernel<kFixed, true> : decode_mfma_kernel<kFixed, false, true>;
   k<<<dim3(n_splits, c.batch), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), n_splits, split_tokens, nullptr, o_part, lse_part);
@@ -856,7 +859,9 @@ hipError_t launch_decode_mfma_balanced(const Dims& d, const Cache& c, const void
                                        float* o_part, float* lse_part, hipStream_t s, bool fp8) {
   (void)d;
   const int tpp_log2 = __builtin_ctz(unsigned(c.page_size / kTile));
-  auto k = fp8 ? decode_mfma_kernel<kBalanced, true> : decode_mfma_kernel<kBalanced, false>;
+  auto k = fp8        ? decode_mfma_kernel<kBalanced, true>
+           : group == 1 ? decode_mfma_kernel<kBalanced, false, true>
+                        : decode_mfma_kernel<kBalanced, false, false>;
   k<<<dim3(n_units), kThreads, 0, s>>>(
       static_cast<const uint16_t*>(c.pool), c.page_table, c.seq_lens, c.batch, c.max_pages, c.page_size, tpp_log2,
       static_cast<const uint16_t*>(q_hat), n_units, group, nullptr, o_part, lse_part);
